@@ -1,0 +1,36 @@
+"""Plain, slow, fp64 CPU oracle for the paged-KV-cache attention path.
+
+TEST INFRASTRUCTURE ONLY. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or call anything here. The HIP
+library and its Python binding never import this package, and this package
+imports nothing from them: the two share no code, tables or helpers.
+
+Every function computes the plain definition of what the path computes, with
+no blocking, fusion or reordering:
+
+* the KV store copies each new token's K and V rows to the cache slot that the
+  slot mapping names (page "nano-vLLM 最小化vLLM重新实现", section 5 "注意力机制",
+  which describes the store kernel writing K/V into the paged cache through
+  ``slot_mapping``);
+* attention is ``softmax(q kᵀ / sqrt(head_dim)) v`` (page at
+  bxzpzcl.cn/news/2159246, section 2.2.2 "两级注意力加速", the manual-attention
+  fallback), with K and V gathered row by row through each sequence's block
+  list (page "nano-vLLM 最小化vLLM重新实现", section 3 "块管理器" and section 4
+  "模型运行器" for the ``[num_blocks, block_size, num_kv_heads, head_dim]``
+  cache), in fp64.
+
+Every function here is pinned by ``tests/test_oracle.py`` against closed forms,
+invariants, a hand-worked golden example, a pure-Python brute force and
+``torch.nn.functional.scaled_dot_product_attention``; none is "parity
+unpinned".
+"""
+
+from .paged_attention import (  # noqa: F401
+    bf16_to_f64,
+    slot_of,
+    store_kvcache,
+    gather_rows,
+    attention_rows,
+    decode,
+    prefill_varlen,
+)
