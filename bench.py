@@ -1,0 +1,213 @@
+"""Benchmark of the paged-KV-cache attention path on one MI355X.
+
+One step is one pass of the whole path over seeded synthetic batches:
+  decode leg   store 256 new tokens + paged decode (256 seqs, L ~ U{100..2048},
+               Hq 16 / Hkv 8 / D 128, 256-token blocks, 4096-block pool);
+  prefill leg  store + causal varlen prefill over packed q/k/v (about 29 seqs
+               of 100..1024 tokens, at most 16384 tokens);
+  prefix leg   store + prefix-cached prefill through the block table (32 seqs
+               sharing 1024 cached tokens, 128..512 new tokens each).
+Inputs are resident in HBM before timing starts. `value` is the decode leg's
+KV-read throughput (bytes of K and V the decode must read, over the leg's
+time); the prefill legs report TFLOP/s of unmasked query-key pairs. Kernel
+times come from HIP events recorded on the launch stream around each call.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attn KV-read GB/s (% HBM peak); prefill attn TFLOP/s (% MFMA)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+
+
+def decode_bytes(wl) -> dict:
+    """Algorithmic bytes of one decode launch: every context token's K and V row
+    of the kv heads, plus q in, out, the used table entries and the lengths."""
+    row = wl.num_kv_heads * wl.head_dim * 2
+    kv = int(wl.context_lens.astype(np.int64).sum()) * row * 2
+    qo = wl.num_seqs * wl.num_q_heads * wl.head_dim * 2 * 2
+    tables = sum(-(-int(n) // wl.block_size) for n in wl.context_lens) * 4
+    return {"kv": kv, "total": kv + qo + tables + wl.num_seqs * 4}
+
+
+def store_bytes(wl, n_tokens) -> int:
+    row = wl.num_kv_heads * wl.head_dim * 2
+    return n_tokens * (2 * row * 2 + 4)
+
+
+def prefill_flops(wl, causal=True) -> int:
+    """4 * D * Hq flops per unmasked (query, key) pair (q.k and p.v)."""
+    nq = np.diff(wl.cu_seqlens_q).astype(np.int64)
+    nk = np.diff(wl.cu_seqlens_k).astype(np.int64)
+    pairs = 0
+    for a, b in zip(nq, nk):
+        pairs += int((b - a) * a + a * (a + 1) // 2) if causal else int(a * b)
+    return pairs * 4 * wl.head_dim * wl.num_q_heads
+
+
+def cpu_baseline(batch, wl, budget_s=15.0):
+    """The fp64 oracle on a bounded prefix of the decode batch, on the host."""
+    import threadpoolctl
+
+    import oracle
+    from tests.parity import Compact  # test infrastructure, used only for this leg
+    from workloads import tensors
+
+    scale = 1.0 / math.sqrt(wl.head_dim)
+    q = tensors.to_u16(batch.q)
+    k_new, v_new = tensors.to_u16(batch.k_new), tensors.to_u16(batch.v_new)
+    slots = batch.slot_mapping.cpu().numpy()
+    done, elapsed, kv = 0, 0.0, 0
+    with threadpoolctl.threadpool_limits(1):
+        while done < wl.num_seqs and elapsed < budget_s:
+            seqs = list(range(done, min(done + 8, wl.num_seqs)))
+            host = Compact(batch, seqs)
+            t0 = time.perf_counter()
+            host.store(k_new, v_new, slots, wl.block_size)
+            oracle.decode(q[seqs], host.k, host.v, host.tables, wl.context_lens[seqs], scale)
+            elapsed += time.perf_counter() - t0
+            kv += int(wl.context_lens[seqs].astype(np.int64).sum()) * wl.num_kv_heads * wl.head_dim * 4
+            done = seqs[-1] + 1
+    return {"value": kv / elapsed / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"store + decode of the first {done} of {wl.num_seqs} sequences of the decode batch "
+                      f"({kv / 1e9:.3f} GB of K/V) in {elapsed:.1f} s, numpy fp64 with one BLAS thread"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--partition", type=int, default=0, help="decode split-K partition (0 = library choice)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this build measures one GPU only; the path is data-parallel and shards by "
+                                   "sequence or kv head with no exchange, so run one process per GPU",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+
+    import paged_kv_cache_heads_amd as pa
+    from workloads import configs, tensors
+
+    dev = torch.device("cuda:0")
+    pa._lib.load()
+    scale = 1.0 / math.sqrt(128)
+
+    wl2, wl3, wl4 = configs.config2(), configs.config3(), configs.config4()
+    b2 = tensors.materialize(wl2, dev)
+    b3 = tensors.materialize(wl3, dev)
+    b4 = tensors.materialize(wl4, dev)
+    ws_bytes = pa.pa_decode_workspace_size(wl2.num_seqs, 16, 8, 128, wl2.max_context_len, args.partition)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    out2 = torch.empty((wl2.num_seqs, 16, 128), dtype=torch.bfloat16, device=dev)
+    out3 = torch.empty((wl3.num_tokens, 16, 128), dtype=torch.bfloat16, device=dev)
+    out4 = torch.empty((wl4.num_tokens, 16, 128), dtype=torch.bfloat16, device=dev)
+    mq3, mq4, mk2 = wl3.max_seqlen_q, wl4.max_seqlen_q, wl2.max_context_len
+
+    kernels = ["store_decode", "decode", "store_prefill", "prefill", "store_prefix", "prefill_prefix"]
+    calls = {
+        "store_decode": lambda: pa.pa_store_kvcache(b2.k_new, b2.v_new, b2.k_cache, b2.v_cache, b2.slot_mapping),
+        "decode": lambda: pa.pa_decode(b2.q, b2.k_cache, b2.v_cache, b2.block_tables, b2.context_lens, scale, mk2,
+                                       out=out2, workspace=ws, partition_tokens=args.partition),
+        "store_prefill": lambda: pa.pa_store_kvcache(b3.k_new, b3.v_new, b3.k_cache, b3.v_cache, b3.slot_mapping),
+        "prefill": lambda: pa.pa_prefill_varlen(b3.q, b3.k_new, b3.v_new, b3.cu_seqlens_q, b3.cu_seqlens_k, mq3,
+                                                scale, out=out3),
+        "store_prefix": lambda: pa.pa_store_kvcache(b4.k_new, b4.v_new, b4.k_cache, b4.v_cache, b4.slot_mapping),
+        "prefill_prefix": lambda: pa.pa_prefill_varlen(b4.q, b4.k_cache, b4.v_cache, b4.cu_seqlens_q,
+                                                       b4.cu_seqlens_k, mq4, scale, block_table=b4.block_tables,
+                                                       out=out4),
+    }
+
+    def step(events=None, i=0):
+        for n, name in enumerate(kernels):
+            if events is not None:
+                events[i][n][0].record()
+            calls[name]()
+            if events is not None:
+                events[i][n][1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in kernels]
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(ev, i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = {name: float(np.mean([ev[i][n][0].elapsed_time(ev[i][n][1]) for i in range(args.steps)]))
+          for n, name in enumerate(kernels)}
+
+    dbytes = decode_bytes(wl2)
+    decode_leg_ms = ms["store_decode"] + ms["decode"]
+    value = dbytes["kv"] / (decode_leg_ms * 1e-3) / 1e9
+    achieved = dbytes["total"] / (ms["decode"] * 1e-3) / 1e9
+    f3, f4 = prefill_flops(wl3), prefill_flops(wl4)
+    t3 = f3 / (ms["prefill"] * 1e-3) / 1e12
+    t4 = f4 / (ms["prefill_prefix"] * 1e-3) / 1e12
+    sb = {"store_decode": store_bytes(wl2, wl2.num_seqs), "store_prefill": store_bytes(wl3, wl3.num_tokens),
+          "store_prefix": store_bytes(wl4, wl4.num_tokens)}
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "decode step of 256 seqs, context U{100..2048} (Hq 16, Hkv 8, D 128, 256-token blocks, "
+                        "4096-block pool) + varlen causal prefill (%d seqs, %d tokens) + prefix-cached prefill "
+                        "(32 seqs, 1024 shared + %d new tokens)" % (wl3.num_seqs, wl3.num_tokens, wl4.num_tokens),
+            "decode_kv_bytes": dbytes["kv"],
+            "decode_partition_tokens": pa.pa_decode_partition_tokens(wl2.num_seqs, 8, mk2, args.partition),
+            "prefill_flops": f3,
+            "prefix_prefill_flops": f4,
+        },
+        "roofline": {"bound": "hbm", "kernel": "pa_decode (partition + reduce kernels)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": dbytes["total"], "avg_launch_us": round(ms["decode"] * 1e3, 2)},
+        "roofline_prefill": {"bound": "mfma", "kernel": "prefill_kernel (varlen, packed)", "achieved": round(t3, 1),
+                             "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                             "frac": round(t3 / MFMA_BF16_PEAK_TFLOPS, 4),
+                             "avg_launch_us": round(ms["prefill"] * 1e3, 2)},
+        "roofline_prefix_prefill": {"bound": "mfma", "kernel": "prefill_kernel (block table)",
+                                    "achieved": round(t4, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                    "frac": round(t4 / MFMA_BF16_PEAK_TFLOPS, 4),
+                                    "avg_launch_us": round(ms["prefill_prefix"] * 1e3, 2)},
+        "kernels_us": {k: round(v * 1e3, 2) for k, v in ms.items()},
+        "store_GBs": {k: round(sb[k] / (ms[k] * 1e-3) / 1e9, 1) for k in sb},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(b2, wl2)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,178 @@
+/*
+ * pa.h — C ABI of the paged-KV-cache attention library for AMD MI355X (gfx950).
+ *
+ * Three operations make up the path, as the nano-vLLM pages describe it:
+ *   pa_store_kvcache   write new tokens' K/V rows into the paged cache by slot;
+ *   pa_decode          one query per sequence against its paged K/V;
+ *   pa_prefill_varlen  causal attention over packed variable-length sequences,
+ *                      K/V packed or read through a block table (prefix cache).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers named *_host are host memory; every other pointer is device
+ *   memory on the current HIP device. bf16 tensors are passed as raw 16-bit
+ *   storage. Strides are in elements.
+ * - A per-layer cache is [num_blocks, block_size, num_kv_heads, head_dim],
+ *   contiguous (page "nano-vLLM 最小化vLLM重新实现", section 4 "模型运行器": one
+ *   KV tensor [2, num_layers, num_blocks, block_size, num_kv_heads, head_dim],
+ *   a layer's K cache and V cache being two of its slices). A flat slot s
+ *   names row s % block_size of block s / block_size.
+ * - Grouped-query attention: query head h reads kv head h / G with
+ *   G = num_q_heads / num_kv_heads (the pages fix only the head counts; this
+ *   contiguous grouping is the library's reading).
+ * - Supported shapes: head_dim == 128; G in {1, 2, 4, 8}; block_size a
+ *   positive multiple of 64 (the pages' default is 256 and they require a
+ *   multiple of 256: page "nano-vLLM 最小化vLLM重新实现", "关键设计选择").
+ *   All pointers and row strides must be 16-byte aligned.
+ * - Ownership: the caller owns every buffer. The library allocates nothing,
+ *   keeps no pointer after return and has no global mutable state. Work is
+ *   enqueued on `stream` (a hipStream_t; NULL = the null stream) and the call
+ *   returns without synchronising; buffers must stay alive until the stream
+ *   has run the work. No entry point reads device memory from the host, so
+ *   all of them may be recorded into a HIP graph.
+ * - Errors: arguments are checked on the host before anything is launched; a
+ *   failed check returns a non-zero pa_status and launches nothing. A launch
+ *   failure returns PA_ERR_HIP. pa_last_error() gives a message for the most
+ *   recent failing call on the calling thread. Device-side preconditions
+ *   (slot and table entries in range, lengths within the stated maxima) are
+ *   the caller's and are not checked on the device.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_NULL_POINTER = 1,        /* a required pointer is NULL */
+  PA_ERR_INVALID_ARGUMENT = 2,    /* negative size, head counts that do not divide, stride too small ... */
+  PA_ERR_UNSUPPORTED = 3,         /* valid but not implemented: head_dim, group size, block_size */
+  PA_ERR_ALIGNMENT = 4,           /* pointer or stride not 16-byte aligned */
+  PA_ERR_WORKSPACE_TOO_SMALL = 5, /* decode workspace smaller than pa_decode_workspace_size() */
+  PA_ERR_HIP = 6                  /* the HIP runtime reported an error at launch */
+} pa_status;
+
+/* Static description of a status code; never NULL. */
+const char* pa_status_string(int status);
+
+/* Message describing the last failing call on this thread ("" if none). */
+const char* pa_last_error(void);
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+int pa_version(void);
+
+/*
+ * pa_store_kvcache — scatter new tokens' K and V rows into the paged cache.
+ *
+ * Page "nano-vLLM 最小化vLLM重新实现", section 5 "注意力机制": the store kernel
+ * writes K/V into the paged cache at the slots given by slot_mapping. For each
+ * token t with slot_mapping[t] = s >= 0:
+ *   k_cache[s / block_size, s % block_size, :, :] = k[t, :, :]
+ *   v_cache[s / block_size, s % block_size, :, :] = v[t, :, :]
+ * Tokens with a negative slot are skipped (padding).
+ *
+ * k, v          [num_tokens, num_kv_heads, head_dim] bf16; heads x dims
+ *               contiguous, token rows k_token_stride / v_token_stride
+ *               elements apart (>= num_kv_heads * head_dim; K and V may be
+ *               column slices of a fused qkv projection output).
+ * k_cache, v_cache  [num_blocks, block_size, num_kv_heads, head_dim] bf16.
+ * slot_mapping  [num_tokens] int32. Non-negative slots must be
+ *               < num_blocks * block_size and pairwise distinct (with a
+ *               repeated slot the result is unspecified).
+ * Bytes copied are exact (bit-for-bit), NaN patterns included.
+ */
+int pa_store_kvcache(const void* k, int64_t k_token_stride, const void* v, int64_t v_token_stride, void* k_cache,
+                     void* v_cache, const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                     int32_t head_dim, int64_t num_blocks, int32_t block_size, void* stream);
+
+/*
+ * pa_decode_workspace_size — bytes of device workspace pa_decode needs.
+ *
+ * Host-only and pure. partition_tokens is the split-K partition length
+ * (0 = the library's choice, else a positive multiple of 256). The same
+ * arguments must be passed to pa_decode. Returns 0 for invalid arguments.
+ */
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                int32_t max_context_len, int32_t partition_tokens);
+
+/* Partition length pa_decode uses for these arguments (0 if invalid). */
+int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
+                                   int32_t partition_tokens);
+
+/*
+ * pa_decode — paged GQA decode attention.
+ *
+ * Page "nano-vLLM 最小化vLLM重新实现", section 5 "注意力机制" (decode attention
+ * reading the paged KV cache) and page at bxzpzcl.cn/news/2159246, section
+ * 2.2.2 (attention = softmax(q kᵀ * scale) v). For sequence b with
+ * L = context_lens[b] and query head h:
+ *   out[b, h, :] = sum_t w_t v_t,  w = softmax_t(scale * q[b, h] . k_t),
+ * over positions t = 0 .. L-1, k_t / v_t being row t % block_size of block
+ * block_tables[b, t / block_size], kv head h / G. L counts the token just
+ * stored, so a new token attends to itself. L == 0 gives a zero row.
+ * Arithmetic: bf16 inputs, fp32 accumulation and softmax, bf16 output
+ * (round to nearest even).
+ *
+ * out           [num_seqs, num_q_heads, head_dim] bf16, contiguous.
+ * q             [num_seqs, num_q_heads, head_dim] bf16; heads x dims
+ *               contiguous, rows q_seq_stride elements apart.
+ * k_cache, v_cache  as in pa_store_kvcache.
+ * block_tables  [num_seqs, max_blocks_per_seq] int32; entries past
+ *               ceil(L / block_size) are never read.
+ * context_lens  [num_seqs] int32, each in [0, max_context_len].
+ * scale         softmax scale (1/sqrt(head_dim) for the pages' models).
+ * workspace     device buffer of at least pa_decode_workspace_size(...) bytes
+ *               (may be NULL when that size is 0); contents undefined after
+ *               the call; must not be shared by work running concurrently.
+ */
+int pa_decode(void* out, const void* q, int64_t q_seq_stride, const void* k_cache, const void* v_cache,
+              const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+              int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+              int32_t max_context_len, float scale, int32_t partition_tokens, void* workspace,
+              size_t workspace_bytes, void* stream);
+
+/*
+ * pa_prefill_varlen — attention over packed variable-length sequences.
+ *
+ * Page "nano-vLLM 最小化vLLM重新实现", section 5 "注意力机制": prefill over
+ * variable-length sequences split by cu_seqlens, with an optional block table
+ * so that prefix-cached blocks are reused (page at hotelren.com/news/2273631,
+ * section 4.4: only the part after the cached prefix is computed).
+ * Sequence i has nq = cu_seqlens_q[i+1] - cu_seqlens_q[i] queries and
+ * nk = cu_seqlens_k[i+1] - cu_seqlens_k[i] keys, nk >= nq. With causal != 0,
+ * query j sits at position nk - nq + j and sees keys 0 .. nk - nq + j (the
+ * queries are the last nq positions); with causal == 0 it sees all nk keys.
+ *   out[q_i + j, h, :] = softmax_t(scale * q[q_i + j, h] . k_t) . v_t
+ * with kv head h / G. Arithmetic: bf16 inputs, bf16 MFMA with fp32
+ * accumulation for q.k and p.v, fp32 softmax, p rounded to bf16 for the p.v
+ * product, bf16 output.
+ *
+ * out           [total_q, num_q_heads, head_dim] bf16, contiguous.
+ * q             [total_q, num_q_heads, head_dim] bf16, rows q_token_stride apart.
+ * k, v          block_table == NULL: packed [total_k, num_kv_heads, head_dim]
+ *               bf16, rows k_token_stride / v_token_stride apart, sequence i's
+ *               keys at rows cu_seqlens_k[i] ..;
+ *               block_table != NULL: the caches [num_blocks, block_size,
+ *               num_kv_heads, head_dim] (the strides are then ignored), key
+ *               t of sequence i at row t % block_size of block
+ *               block_table[i, t / block_size].
+ * cu_seqlens_q, cu_seqlens_k  [num_seqs + 1] int32, non-decreasing from 0.
+ * max_seqlen_q  upper bound of every nq (sizes the launch grid).
+ * block_table   optional [num_seqs, max_blocks_per_seq] int32.
+ */
+int pa_prefill_varlen(void* out, const void* q, int64_t q_token_stride, const void* k, const void* v,
+                      int64_t k_token_stride, int64_t v_token_stride, const int32_t* cu_seqlens_q,
+                      const int32_t* cu_seqlens_k, int32_t num_seqs, int32_t max_seqlen_q, int32_t num_q_heads,
+                      int32_t num_kv_heads, int32_t head_dim, float scale, int32_t causal,
+                      const int32_t* block_table, int32_t max_blocks_per_seq, int32_t block_size, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

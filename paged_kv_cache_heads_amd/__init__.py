@@ -1,0 +1,135 @@
+"""Python binding of libpa.so, the paged-KV-cache attention library for MI355X.
+
+Argument marshalling only: every function passes tensor addresses, strides and
+sizes to the C entry point of the same name in include/pa.h, on the current
+HIP stream, and raises PAError if it returns a non-zero status. All compute
+runs in the library's HIP kernels; there is no fallback path.
+
+Tensors are torch tensors on the GPU: bf16 data, int32 metadata.
+"""
+
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+from ._lib import LibraryMissing  # noqa: F401
+
+__all__ = [
+    "PAError", "LibraryMissing", "pa_store_kvcache", "pa_decode", "pa_decode_workspace_size",
+    "pa_decode_partition_tokens", "pa_prefill_varlen", "pa_status_string", "pa_last_error", "pa_version",
+    "library_path",
+]
+
+
+class PAError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        lib = _lib.load()
+        self.status = status
+        msg = lib.pa_last_error().decode() or lib.pa_status_string(status).decode()
+        super().__init__(f"{fn} failed with status {status} ({lib.pa_status_string(status).decode()}): {msg}")
+
+
+def library_path() -> str:
+    return _lib.LIB_PATH
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise PAError(fn, status)
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else t.data_ptr()
+
+
+def _stream(stream, device) -> int:
+    if stream is not None:
+        return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _rows(t: torch.Tensor, name: str) -> int:
+    """Row stride (elements) of a [rows, heads, dims] view whose heads x dims are contiguous."""
+    if t.dim() != 3 or t.stride(2) != 1 or t.stride(1) != t.shape[2]:
+        raise ValueError(f"{name} must be [rows, heads, dims] with contiguous heads x dims, got "
+                         f"shape {tuple(t.shape)} strides {t.stride()}")
+    return t.stride(0)
+
+
+def pa_status_string(status: int) -> str:
+    return _lib.load().pa_status_string(status).decode()
+
+
+def pa_last_error() -> str:
+    return _lib.load().pa_last_error().decode()
+
+
+def pa_version() -> int:
+    return _lib.load().pa_version()
+
+
+def pa_store_kvcache(k, v, k_cache, v_cache, slot_mapping, stream=None) -> None:
+    """Write k[t] / v[t] ([T, Hkv, D] bf16) into the caches ([NB, bs, Hkv, D]) at slot_mapping[t]."""
+    lib = _lib.load()
+    nb, bs, hkv, d = k_cache.shape
+    _check("pa_store_kvcache", lib.pa_store_kvcache(
+        _ptr(k), _rows(k, "k"), _ptr(v), _rows(v, "v"), _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping),
+        int(slot_mapping.shape[0]), hkv, d, nb, bs, _stream(stream, k_cache.device)))
+
+
+def pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                             partition_tokens=0) -> int:
+    return int(_lib.load().pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                    max_context_len, partition_tokens))
+
+
+def pa_decode_partition_tokens(num_seqs, num_kv_heads, max_context_len, partition_tokens=0) -> int:
+    return int(_lib.load().pa_decode_partition_tokens(num_seqs, num_kv_heads, max_context_len, partition_tokens))
+
+
+def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, max_context_len: int, out=None,
+              workspace=None, partition_tokens: int = 0, stream=None):
+    """Paged decode: q [B, Hq, D] bf16 -> out [B, Hq, D] bf16.
+
+    workspace: a uint8 device tensor of at least pa_decode_workspace_size(...)
+    bytes; allocated here when not given.
+    """
+    lib = _lib.load()
+    b, hq, d = q.shape
+    nb, bs, hkv, _ = k_cache.shape
+    if out is None:
+        out = torch.empty((b, hq, d), dtype=torch.bfloat16, device=q.device)
+    need = lib.pa_decode_workspace_size(b, hq, hkv, d, max_context_len, partition_tokens)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("pa_decode", lib.pa_decode(
+        _ptr(out), _ptr(q), _rows(q, "q"), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+        int(block_tables.shape[1]), _ptr(context_lens), b, hq, hkv, d, bs, int(max_context_len), float(scale),
+        int(partition_tokens), _ptr(workspace), ws_bytes, _stream(stream, q.device)))
+    return out
+
+
+def pa_prefill_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, scale: float, causal: bool = True,
+                      block_table=None, out=None, stream=None):
+    """Varlen prefill: q [Tq, Hq, D] bf16 -> out [Tq, Hq, D] bf16.
+
+    Without block_table, k / v are packed [Tk, Hkv, D] (row strides may exceed
+    Hkv * D); with it, k / v are the caches [NB, bs, Hkv, D].
+    """
+    lib = _lib.load()
+    tq, hq, d = q.shape
+    if out is None:
+        out = torch.empty((tq, hq, d), dtype=torch.bfloat16, device=q.device)
+    if block_table is None:
+        hkv = k.shape[1]
+        ks, vs, width, bs = _rows(k, "k"), _rows(v, "v"), 0, 0
+    else:
+        _, bs, hkv, _ = k.shape
+        ks, vs, width = hkv * d, hkv * d, int(block_table.shape[1])
+    _check("pa_prefill_varlen", lib.pa_prefill_varlen(
+        _ptr(out), _ptr(q), _rows(q, "q"), _ptr(k), _ptr(v), ks, vs, _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+        int(cu_seqlens_q.shape[0]) - 1, int(max_seqlen_q), hq, hkv, d, float(scale), 1 if causal else 0,
+        _ptr(block_table), width, bs, _stream(stream, q.device)))
+    return out

@@ -1,0 +1,46 @@
+"""ctypes loader for libpa.so and the signatures of include/pa.h."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libpa.so")
+
+_i32, _i64, _vp, _sz, _f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_float
+_i32p = ctypes.c_void_p  # int32 device pointers travel as addresses
+
+SIGNATURES = {
+    "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "pa_last_error": (ctypes.c_char_p, []),
+    "pa_version": (ctypes.c_int, []),
+    "pa_store_kvcache": (ctypes.c_int, [_vp, _i64, _vp, _i64, _vp, _vp, _i32p, _i32, _i32, _i32, _i64, _i32, _vp]),
+    "pa_decode_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "pa_decode_partition_tokens": (_i32, [_i32, _i32, _i32, _i32]),
+    "pa_decode": (ctypes.c_int, [_vp, _vp, _i64, _vp, _vp, _i32p, _i32, _i32p, _i32, _i32, _i32, _i32, _i32, _i32,
+                                 _f32, _i32, _vp, _sz, _vp]),
+    "pa_prefill_varlen": (ctypes.c_int, [_vp, _vp, _i64, _vp, _vp, _i64, _i64, _i32p, _i32p, _i32, _i32, _i32, _i32,
+                                         _i32, _f32, _i32, _i32p, _i32, _i32, _vp]),
+}
+
+_LIB = None
+
+
+class LibraryMissing(RuntimeError):
+    pass
+
+
+def load() -> ctypes.CDLL:
+    """Load libpa.so once. Raises LibraryMissing if it has not been built."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise LibraryMissing(f"{LIB_PATH} is missing: build it with `python -m paged_kv_cache_heads_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = lib
+    return _LIB

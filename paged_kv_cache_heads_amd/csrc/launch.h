@@ -1,0 +1,71 @@
+// Host-side launchers of the kernels (internal to the library). The public
+// C ABI in include/pa.h validates arguments, then calls these.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+struct StoreArgs {
+  const uint16_t* k;
+  const uint16_t* v;
+  int64_t k_token_stride;  // elements
+  int64_t v_token_stride;  // elements
+  uint16_t* k_cache;
+  uint16_t* v_cache;
+  const int32_t* slot_mapping;
+  int32_t num_tokens;
+  int32_t row_vecs;  // 16-byte vectors per token row (num_kv_heads * head_dim / 8)
+};
+
+struct DecodeArgs {
+  uint16_t* out;
+  const uint16_t* q;
+  int64_t q_seq_stride;
+  const uint16_t* k_cache;
+  const uint16_t* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  float* ws_o;   // [num_seqs, num_q_heads, num_partitions, head_dim]
+  float* ws_ml;  // [num_seqs, num_q_heads, num_partitions, 2]  (max, sum)
+  int32_t max_blocks_per_seq;
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t block_size;
+  int32_t partition;       // tokens per partition (multiple of 256)
+  int32_t num_partitions;  // ceil(max_context_len / partition)
+  float scale_log2e;
+};
+
+struct PrefillArgs {
+  uint16_t* out;
+  const uint16_t* q;
+  int64_t q_token_stride;
+  const uint16_t* k;
+  const uint16_t* v;
+  int64_t k_token_stride;
+  int64_t v_token_stride;
+  const int32_t* cu_seqlens_q;
+  const int32_t* cu_seqlens_k;
+  const int32_t* block_table;  // null: packed k/v
+  int32_t max_blocks_per_seq;
+  int32_t block_size;
+  int32_t num_seqs;
+  int32_t num_q_tiles;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t causal;
+  float scale_log2e;
+};
+
+hipError_t launch_store_kvcache(const StoreArgs& a, hipStream_t stream);
+// group = num_q_heads / num_kv_heads (1, 2, 4 or 8); head_dim is 128.
+hipError_t launch_decode(const DecodeArgs& a, int group, hipStream_t stream);
+hipError_t launch_prefill(const PrefillArgs& a, int group, hipStream_t stream);
+
+// Query positions covered by one prefill workgroup for a GQA group size.
+inline int prefill_tile_positions(int group) { return 128 / group; }
+
+}  // namespace pa

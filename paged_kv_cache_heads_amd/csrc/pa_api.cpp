@@ -1,0 +1,287 @@
+// Host side of the C ABI declared in include/pa.h: argument checks, launch
+// geometry (decode partition length, prefill tile count) and error mapping.
+// Nothing here reads device memory, so every entry point is graph-capturable.
+#include "../../include/pa.h"
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "launch.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_last_error[0] = '\0';
+  return PA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int kHeadDim = 128;
+constexpr float kLog2e = 1.4426950408889634f;
+
+bool supported_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8; }
+
+// Checks shared by the attention entry points.
+int check_heads(int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim) {
+  if (num_q_heads <= 0 || num_kv_heads <= 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "num_q_heads (%d) and num_kv_heads (%d) must be positive", num_q_heads,
+                num_kv_heads);
+  if (num_q_heads % num_kv_heads != 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "num_q_heads (%d) is not a multiple of num_kv_heads (%d)", num_q_heads,
+                num_kv_heads);
+  if (head_dim != kHeadDim) return fail(PA_ERR_UNSUPPORTED, "head_dim %d unsupported (only 128)", head_dim);
+  if (!supported_group(num_q_heads / num_kv_heads))
+    return fail(PA_ERR_UNSUPPORTED, "GQA group %d unsupported (1, 2, 4 or 8)", num_q_heads / num_kv_heads);
+  return PA_OK;
+}
+
+int check_block_size(int32_t block_size) {
+  if (block_size <= 0) return fail(PA_ERR_INVALID_ARGUMENT, "block_size %d must be positive", block_size);
+  if (block_size % 64 != 0) return fail(PA_ERR_UNSUPPORTED, "block_size %d is not a multiple of 64", block_size);
+  return PA_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Split-K partition length (tokens). Chosen from sizes known on the host only.
+int32_t choose_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len, int32_t requested) {
+  if (requested > 0) return requested;
+  (void)num_seqs;
+  (void)num_kv_heads;
+  int32_t p = 512;
+  // keep the partition count per sequence at or below 64
+  while ((int64_t)p * 64 < (int64_t)max_context_len) p *= 2;
+  return p;
+}
+
+struct DecodeGeometry {
+  int32_t partition;
+  int32_t num_partitions;
+  size_t ws_o_bytes;
+  size_t ws_bytes;
+};
+
+bool decode_geometry(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t max_context_len,
+                     int32_t partition_tokens, DecodeGeometry* g) {
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_context_len < 0) return false;
+  if (partition_tokens < 0 || partition_tokens % 256 != 0) return false;
+  g->partition = choose_partition(num_seqs, num_kv_heads, max_context_len, partition_tokens);
+  g->num_partitions = max_context_len == 0 ? 1 : (max_context_len + g->partition - 1) / g->partition;
+  if (g->num_partitions <= 1) {
+    g->ws_o_bytes = 0;
+    g->ws_bytes = 0;
+    return true;
+  }
+  const size_t slots = (size_t)num_seqs * num_q_heads * g->num_partitions;
+  g->ws_o_bytes = slots * kHeadDim * sizeof(float);
+  g->ws_bytes = g->ws_o_bytes + slots * 2 * sizeof(float);
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_string(int status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_NULL_POINTER: return "null pointer";
+    case PA_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case PA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case PA_ERR_ALIGNMENT: return "misaligned pointer or stride";
+    case PA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case PA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* pa_last_error(void) { return g_last_error; }
+
+int pa_version(void) { return 100; }
+
+int pa_store_kvcache(const void* k, int64_t k_token_stride, const void* v, int64_t v_token_stride, void* k_cache,
+                     void* v_cache, const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                     int32_t head_dim, int64_t num_blocks, int32_t block_size, void* stream) {
+  if (num_tokens < 0) return fail(PA_ERR_INVALID_ARGUMENT, "num_tokens %d is negative", num_tokens);
+  if (num_kv_heads <= 0 || head_dim <= 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "num_kv_heads (%d) and head_dim (%d) must be positive", num_kv_heads,
+                head_dim);
+  if (num_blocks <= 0 || block_size <= 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "num_blocks (%lld) and block_size (%d) must be positive",
+                (long long)num_blocks, block_size);
+  const int64_t row = (int64_t)num_kv_heads * head_dim;
+  if (row % 8 != 0) return fail(PA_ERR_ALIGNMENT, "a token row (%lld elements) is not a multiple of 16 bytes",
+                                (long long)row);
+  if (num_blocks * (int64_t)block_size > INT32_MAX)
+    return fail(PA_ERR_UNSUPPORTED, "num_blocks * block_size exceeds the int32 slot range");
+  if (num_tokens == 0) return ok();
+  if (!k || !v || !k_cache || !v_cache || !slot_mapping)
+    return fail(PA_ERR_NULL_POINTER, "k, v, k_cache, v_cache and slot_mapping are required");
+  if (k_token_stride < row || v_token_stride < row)
+    return fail(PA_ERR_INVALID_ARGUMENT, "token strides (%lld, %lld) are below a row (%lld)",
+                (long long)k_token_stride, (long long)v_token_stride, (long long)row);
+  if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache) || k_token_stride % 8 ||
+      v_token_stride % 8)
+    return fail(PA_ERR_ALIGNMENT, "k, v, caches and token strides must be 16-byte aligned");
+  if ((uint64_t)num_tokens * 2u * (uint64_t)(row / 8) > 0xFFFFFFFFull)
+    return fail(PA_ERR_UNSUPPORTED, "too many tokens for one call");
+  pa::StoreArgs a;
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.k_token_stride = k_token_stride;
+  a.v_token_stride = v_token_stride;
+  a.k_cache = static_cast<uint16_t*>(k_cache);
+  a.v_cache = static_cast<uint16_t*>(v_cache);
+  a.slot_mapping = slot_mapping;
+  a.num_tokens = num_tokens;
+  a.row_vecs = (int32_t)(row / 8);
+  return hip_status(pa::launch_store_kvcache(a, static_cast<hipStream_t>(stream)), "store_kvcache launch");
+}
+
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                int32_t max_context_len, int32_t partition_tokens) {
+  if (head_dim != kHeadDim) return 0;
+  DecodeGeometry g;
+  if (!decode_geometry(num_seqs, num_q_heads, num_kv_heads, max_context_len, partition_tokens, &g)) return 0;
+  return g.ws_bytes;
+}
+
+int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
+                                   int32_t partition_tokens) {
+  DecodeGeometry g;
+  if (!decode_geometry(num_seqs, 1 * num_kv_heads, num_kv_heads, max_context_len, partition_tokens, &g)) return 0;
+  return g.partition;
+}
+
+int pa_decode(void* out, const void* q, int64_t q_seq_stride, const void* k_cache, const void* v_cache,
+              const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+              int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+              int32_t max_context_len, float scale, int32_t partition_tokens, void* workspace,
+              size_t workspace_bytes, void* stream) {
+  if (num_seqs < 0) return fail(PA_ERR_INVALID_ARGUMENT, "num_seqs %d is negative", num_seqs);
+  if (num_seqs > 65535) return fail(PA_ERR_UNSUPPORTED, "num_seqs %d exceeds 65535", num_seqs);
+  int st = check_heads(num_q_heads, num_kv_heads, head_dim);
+  if (st) return st;
+  st = check_block_size(block_size);
+  if (st) return st;
+  if (max_context_len < 0) return fail(PA_ERR_INVALID_ARGUMENT, "max_context_len %d is negative", max_context_len);
+  if (max_blocks_per_seq < 0 || (int64_t)max_blocks_per_seq * block_size < max_context_len)
+    return fail(PA_ERR_INVALID_ARGUMENT, "max_blocks_per_seq (%d) x block_size (%d) < max_context_len (%d)",
+                max_blocks_per_seq, block_size, max_context_len);
+  if (partition_tokens < 0 || partition_tokens % 256 != 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "partition_tokens %d must be 0 or a positive multiple of 256",
+                partition_tokens);
+  if (!(scale == scale) || isinf(scale)) return fail(PA_ERR_INVALID_ARGUMENT, "scale must be finite");
+  if (num_seqs == 0) return ok();
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+    return fail(PA_ERR_NULL_POINTER, "out, q, caches, block_tables and context_lens are required");
+  if (q_seq_stride < (int64_t)num_q_heads * head_dim)
+    return fail(PA_ERR_INVALID_ARGUMENT, "q_seq_stride %lld is below num_q_heads * head_dim",
+                (long long)q_seq_stride);
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || q_seq_stride % 8)
+    return fail(PA_ERR_ALIGNMENT, "out, q, caches and q_seq_stride must be 16-byte aligned");
+  DecodeGeometry g;
+  decode_geometry(num_seqs, num_q_heads, num_kv_heads, max_context_len, partition_tokens, &g);
+  if (g.num_partitions > 65535) return fail(PA_ERR_UNSUPPORTED, "too many partitions (%d)", g.num_partitions);
+  if (g.ws_bytes > 0) {
+    if (!workspace) return fail(PA_ERR_NULL_POINTER, "workspace of %zu bytes is required", g.ws_bytes);
+    if (workspace_bytes < g.ws_bytes)
+      return fail(PA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < required %zu", workspace_bytes, g.ws_bytes);
+    if (!aligned16(workspace)) return fail(PA_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
+  }
+  pa::DecodeArgs a;
+  a.out = static_cast<uint16_t*>(out);
+  a.q = static_cast<const uint16_t*>(q);
+  a.q_seq_stride = q_seq_stride;
+  a.k_cache = static_cast<const uint16_t*>(k_cache);
+  a.v_cache = static_cast<const uint16_t*>(v_cache);
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.ws_o = static_cast<float*>(workspace);
+  a.ws_ml = g.ws_bytes ? reinterpret_cast<float*>(static_cast<char*>(workspace) + g.ws_o_bytes) : nullptr;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.block_size = block_size;
+  a.partition = g.partition;
+  a.num_partitions = g.num_partitions;
+  a.scale_log2e = scale * kLog2e;
+  return hip_status(pa::launch_decode(a, num_q_heads / num_kv_heads, static_cast<hipStream_t>(stream)),
+                    "decode launch");
+}
+
+int pa_prefill_varlen(void* out, const void* q, int64_t q_token_stride, const void* k, const void* v,
+                      int64_t k_token_stride, int64_t v_token_stride, const int32_t* cu_seqlens_q,
+                      const int32_t* cu_seqlens_k, int32_t num_seqs, int32_t max_seqlen_q, int32_t num_q_heads,
+                      int32_t num_kv_heads, int32_t head_dim, float scale, int32_t causal,
+                      const int32_t* block_table, int32_t max_blocks_per_seq, int32_t block_size, void* stream) {
+  if (num_seqs < 0 || max_seqlen_q < 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "num_seqs (%d) and max_seqlen_q (%d) must be >= 0", num_seqs, max_seqlen_q);
+  if (num_seqs > 65535) return fail(PA_ERR_UNSUPPORTED, "num_seqs %d exceeds 65535", num_seqs);
+  int st = check_heads(num_q_heads, num_kv_heads, head_dim);
+  if (st) return st;
+  if (!(scale == scale) || isinf(scale)) return fail(PA_ERR_INVALID_ARGUMENT, "scale must be finite");
+  const int64_t kv_row = (int64_t)num_kv_heads * head_dim;
+  if (block_table) {
+    st = check_block_size(block_size);
+    if (st) return st;
+    if (max_blocks_per_seq <= 0)
+      return fail(PA_ERR_INVALID_ARGUMENT, "max_blocks_per_seq %d must be positive with a block table",
+                  max_blocks_per_seq);
+  } else {
+    if (k_token_stride < kv_row || v_token_stride < kv_row)
+      return fail(PA_ERR_INVALID_ARGUMENT, "k/v token strides (%lld, %lld) are below a row (%lld)",
+                  (long long)k_token_stride, (long long)v_token_stride, (long long)kv_row);
+    if (k_token_stride % 8 || v_token_stride % 8)
+      return fail(PA_ERR_ALIGNMENT, "k/v token strides must be 16-byte aligned");
+  }
+  if (num_seqs == 0 || max_seqlen_q == 0) return ok();
+  if (!out || !q || !k || !v || !cu_seqlens_q || !cu_seqlens_k)
+    return fail(PA_ERR_NULL_POINTER, "out, q, k, v, cu_seqlens_q and cu_seqlens_k are required");
+  if (q_token_stride < (int64_t)num_q_heads * head_dim)
+    return fail(PA_ERR_INVALID_ARGUMENT, "q_token_stride %lld is below num_q_heads * head_dim",
+                (long long)q_token_stride);
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k) || !aligned16(v) || q_token_stride % 8)
+    return fail(PA_ERR_ALIGNMENT, "out, q, k, v and q_token_stride must be 16-byte aligned");
+  const int group = num_q_heads / num_kv_heads;
+  const int qp = pa::prefill_tile_positions(group);
+  pa::PrefillArgs a;
+  a.out = static_cast<uint16_t*>(out);
+  a.q = static_cast<const uint16_t*>(q);
+  a.q_token_stride = q_token_stride;
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.k_token_stride = block_table ? kv_row : k_token_stride;
+  a.v_token_stride = block_table ? kv_row : v_token_stride;
+  a.cu_seqlens_q = cu_seqlens_q;
+  a.cu_seqlens_k = cu_seqlens_k;
+  a.block_table = block_table;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.block_size = block_table ? block_size : 0;
+  a.num_seqs = num_seqs;
+  a.num_q_tiles = (max_seqlen_q + qp - 1) / qp;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.causal = causal ? 1 : 0;
+  a.scale_log2e = scale * kLog2e;
+  return hip_status(pa::launch_prefill(a, group, static_cast<hipStream_t>(stream)), "prefill launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,153 @@
+"""The C ABI without a GPU: the library loads, exports what include/pa.h declares,
+and rejects bad arguments on the host before launching anything.
+
+Every call here fails validation (or is a documented no-op), so no kernel is
+ever launched and no pointer is dereferenced; the fake addresses below are
+never touched.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_kv_cache_heads_amd as pa
+from paged_kv_cache_heads_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pa.h")
+
+PA_OK, NULLP, INVAL, UNSUP, ALIGN, WS = 0, 1, 2, 3, 4, 5
+A = 0x100000  # a 16-byte aligned fake address (never dereferenced)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from paged_kv_cache_heads_amd import build
+        build.build()
+    return _lib.load()
+
+
+def declared_functions():
+    with open(HEADER, encoding="utf-8") as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_entry_points():
+    names = declared_functions()
+    for n in ["pa_store_kvcache", "pa_decode", "pa_decode_workspace_size", "pa_prefill_varlen",
+              "pa_status_string", "pa_last_error"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert name in _lib.SIGNATURES, f"{name} has no ctypes signature"
+
+
+def test_status_strings(lib):
+    for s in range(0, 7):
+        assert lib.pa_status_string(s)
+    assert lib.pa_status_string(99) == b"unknown status"
+    assert lib.pa_version() >= 100
+
+
+def store(lib, **kw):
+    args = dict(k=A, ks=1024, v=A, vs=1024, kc=A, vc=A, slot=A, T=4, hkv=8, d=128, nb=16, bs=256, stream=None)
+    args.update(kw)
+    return lib.pa_store_kvcache(args["k"], args["ks"], args["v"], args["vs"], args["kc"], args["vc"], args["slot"],
+                                args["T"], args["hkv"], args["d"], args["nb"], args["bs"], args["stream"])
+
+
+def test_store_validation(lib):
+    assert store(lib, T=-1) == INVAL
+    assert store(lib, k=None) == NULLP
+    assert store(lib, slot=None) == NULLP
+    assert store(lib, ks=512) == INVAL
+    assert store(lib, k=A + 8) == ALIGN
+    assert store(lib, vs=1028) == ALIGN
+    assert store(lib, nb=0) == INVAL
+    assert store(lib, hkv=3, d=5) == ALIGN
+    assert store(lib, nb=1 << 24, bs=256) == UNSUP
+    assert b"null" in lib.pa_last_error() or lib.pa_last_error()
+    # zero tokens: a no-op that needs no pointers
+    assert store(lib, T=0, k=None, v=None, kc=None, vc=None, slot=None) == PA_OK
+
+
+def decode(lib, **kw):
+    a = dict(out=A, q=A, qs=2048, kc=A, vc=A, bt=A, W=8, cl=A, B=4, hq=16, hkv=8, d=128, bs=256, maxL=2048,
+             scale=0.088, part=0, ws=A, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return lib.pa_decode(a["out"], a["q"], a["qs"], a["kc"], a["vc"], a["bt"], a["W"], a["cl"], a["B"], a["hq"],
+                         a["hkv"], a["d"], a["bs"], a["maxL"], a["scale"], a["part"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_decode_validation(lib):
+    assert decode(lib, hq=12) == INVAL           # 12 % 8
+    assert decode(lib, hq=24) == UNSUP           # group 3
+    assert decode(lib, hq=128) == UNSUP          # group 16
+    assert decode(lib, d=64) == UNSUP
+    assert decode(lib, bs=100) == UNSUP
+    assert decode(lib, bs=0) == INVAL
+    assert decode(lib, W=7) == INVAL             # 7 * 256 < 2048
+    assert decode(lib, B=-1) == INVAL
+    assert decode(lib, B=70000) == UNSUP
+    assert decode(lib, part=100) == INVAL
+    assert decode(lib, scale=float("nan")) == INVAL
+    assert decode(lib, q=None) == NULLP
+    assert decode(lib, cl=None) == NULLP
+    assert decode(lib, qs=1024) == INVAL
+    assert decode(lib, out=A + 2) == ALIGN
+    assert decode(lib, ws=None) == NULLP         # partitions > 1 need a workspace
+    assert decode(lib, wsb=16) == WS
+    assert decode(lib, ws=A + 4) == ALIGN
+    assert decode(lib, B=0, out=None, q=None, kc=None, vc=None, bt=None, cl=None) == PA_OK
+
+
+def test_decode_workspace_size(lib):
+    p = lib.pa_decode_partition_tokens(256, 8, 2048, 0)
+    assert p >= 256 and p % 256 == 0
+    nparts = -(-2048 // p)
+    want = 0 if nparts <= 1 else 256 * 16 * nparts * (128 + 2) * 4
+    assert lib.pa_decode_workspace_size(256, 16, 8, 128, 2048, 0) == want
+    assert lib.pa_decode_workspace_size(256, 16, 8, 128, 2048, 256) == 256 * 16 * 8 * 130 * 4
+    assert lib.pa_decode_workspace_size(4, 16, 8, 128, 200, 256) == 0  # one partition: no workspace
+    assert lib.pa_decode_workspace_size(4, 16, 8, 64, 2048, 0) == 0    # unsupported head_dim
+    assert lib.pa_decode_workspace_size(4, 16, 8, 128, 2048, 100) == 0  # bad partition
+    assert lib.pa_decode_partition_tokens(4, 8, 2048, 768) == 768
+
+
+def prefill(lib, **kw):
+    a = dict(out=A, q=A, qs=2048, k=A, v=A, ks=3072, vs=3072, cq=A, ck=A, S=4, maxq=1024, hq=16, hkv=8, d=128,
+             scale=0.088, causal=1, bt=None, W=0, bs=0, stream=None)
+    a.update(kw)
+    return lib.pa_prefill_varlen(a["out"], a["q"], a["qs"], a["k"], a["v"], a["ks"], a["vs"], a["cq"], a["ck"],
+                                 a["S"], a["maxq"], a["hq"], a["hkv"], a["d"], a["scale"], a["causal"], a["bt"],
+                                 a["W"], a["bs"], a["stream"])
+
+
+def test_prefill_validation(lib):
+    assert prefill(lib, hq=20) == INVAL
+    assert prefill(lib, d=256) == UNSUP
+    assert prefill(lib, S=-2) == INVAL
+    assert prefill(lib, maxq=-1) == INVAL
+    assert prefill(lib, ks=512) == INVAL
+    assert prefill(lib, vs=1028) == ALIGN
+    assert prefill(lib, cq=None) == NULLP
+    assert prefill(lib, qs=1000) == ALIGN or prefill(lib, qs=1000) == INVAL
+    assert prefill(lib, q=A + 6) == ALIGN
+    assert prefill(lib, bt=A, W=0, bs=256) == INVAL
+    assert prefill(lib, bt=A, W=6, bs=96) == UNSUP
+    assert prefill(lib, scale=float("inf")) == INVAL
+    assert prefill(lib, S=0, out=None, q=None, k=None, v=None, cq=None, ck=None) == PA_OK
+
+
+def test_python_binding_reports_errors(lib):
+    with pytest.raises(pa.PAError) as e:
+        pa._check("pa_decode", INVAL)
+    assert "invalid argument" in str(e.value)

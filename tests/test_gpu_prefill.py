@@ -1,0 +1,113 @@
+"""pa_prefill_varlen on the GPU against the oracle (per-element tolerance)."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_heads_amd as pa
+from tests.gpu_common import announce, dev  # noqa: F401
+from tests.parity import Compact, assert_attention_close
+from workloads import configs, tensors
+
+pytestmark = pytest.mark.gpu
+
+
+def _packed(wl, dev, causal=True, check_table_path=True):
+    """Prefill over packed q/k/v; the same keys read back through the cache must give identical bits."""
+    batch = tensors.materialize(wl, dev)
+    scale = 1.0 / math.sqrt(wl.head_dim)
+    pa.pa_store_kvcache(batch.k_new, batch.v_new, batch.k_cache, batch.v_cache, batch.slot_mapping)
+    out = pa.pa_prefill_varlen(batch.q, batch.k_new, batch.v_new, batch.cu_seqlens_q, batch.cu_seqlens_k,
+                               wl.max_seqlen_q, scale, causal=causal)
+    out_t = None
+    if check_table_path:
+        out_t = pa.pa_prefill_varlen(batch.q, batch.k_cache, batch.v_cache, batch.cu_seqlens_q, batch.cu_seqlens_k,
+                                     wl.max_seqlen_q, scale, causal=causal, block_table=batch.block_tables)
+    torch.cuda.synchronize()
+    ref = oracle.prefill_varlen(tensors.to_u16(batch.q), tensors.to_u16(batch.k_new), tensors.to_u16(batch.v_new),
+                                wl.cu_seqlens_q, wl.cu_seqlens_k, scale, causal=causal)
+    stats = assert_attention_close(out, ref, wl.name)
+    if out_t is not None:
+        assert torch.equal(out.view(torch.int16), out_t.view(torch.int16)), "table path differs from packed path"
+    return stats
+
+
+def _table(wl, dev, causal=True):
+    """store the new tokens, then prefill through the block table (prefix blocks shared)."""
+    batch = tensors.materialize(wl, dev)
+    scale = 1.0 / math.sqrt(wl.head_dim)
+    host = Compact(batch, range(wl.num_seqs))  # pre-store contents
+    k_new, v_new = tensors.to_u16(batch.k_new), tensors.to_u16(batch.v_new)
+    slots = batch.slot_mapping.cpu().numpy()
+    pa.pa_store_kvcache(batch.k_new, batch.v_new, batch.k_cache, batch.v_cache, batch.slot_mapping)
+    out = pa.pa_prefill_varlen(batch.q, batch.k_cache, batch.v_cache, batch.cu_seqlens_q, batch.cu_seqlens_k,
+                               wl.max_seqlen_q, scale, causal=causal, block_table=batch.block_tables)
+    torch.cuda.synchronize()
+    host.store(k_new, v_new, slots, wl.block_size)
+    ref = oracle.prefill_varlen(tensors.to_u16(batch.q), host.k, host.v, wl.cu_seqlens_q, wl.cu_seqlens_k, scale,
+                                causal=causal, block_table=host.tables)
+    return assert_attention_close(out, ref, wl.name)
+
+
+@pytest.mark.parametrize("seed", [3, 101])
+def test_prefill_config3(dev, seed):
+    announce(f"prefill config 3 seed {seed}")
+    _packed(configs.config3(seed), dev)
+
+
+@pytest.mark.parametrize("seed", [4, 102])
+def test_prefill_config4(dev, seed):
+    announce(f"prefill config 4 seed {seed}")
+    _table(configs.config4(seed), dev)
+
+
+@pytest.mark.parametrize("group", [1, 2, 4, 8])
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_ragged_small(dev, group, causal):
+    # lengths around tile edges (16, 64, 128/G positions) and single-token sequences
+    lens = [1, 2, 15, 16, 17, 63, 64, 65, 127, 129, 300]
+    announce(f"prefill ragged G={group} causal={causal}")
+    wl = configs.prefill_workload("ragged", lens, 0, 2 * group, 2, 64, seed=21)
+    _packed(wl, dev, causal=causal)
+
+
+@pytest.mark.parametrize("block_size", [64, 256])
+@pytest.mark.parametrize("group", [2, 4])
+def test_prefill_prefix_small(dev, block_size, group):
+    # fewer queries than keys: queries are the last positions; prefix blocks shared
+    announce(f"prefill prefix bs={block_size} G={group}")
+    wl = configs.prefill_workload("prefix", [1, 5, 64, 100, 200], 256, 2 * group, 2, 64, seed=22,
+                                  block_size=block_size)
+    _table(wl, dev, causal=True)
+    _table(wl, dev, causal=False)
+
+
+def test_prefill_empty_sequence_in_batch(dev):
+    announce("prefill with an empty sequence in the batch")
+    wl = configs.prefill_workload("empty", [5, 0, 70], 0, 4, 2, 16, seed=23)
+    _packed(wl, dev)
+
+
+def test_prefill_last_row_equals_decode(dev):
+    # the last query row of each sequence sees the same keys as a decode over that sequence
+    announce("prefill last row vs decode")
+    lens = [1, 77, 256, 300]
+    wl = configs.prefill_workload("lastrow", lens, 0, 16, 8, 16, seed=24)
+    batch = tensors.materialize(wl, dev)
+    scale = 1.0 / math.sqrt(128)
+    pa.pa_store_kvcache(batch.k_new, batch.v_new, batch.k_cache, batch.v_cache, batch.slot_mapping)
+    out = pa.pa_prefill_varlen(batch.q, batch.k_cache, batch.v_cache, batch.cu_seqlens_q, batch.cu_seqlens_k,
+                               wl.max_seqlen_q, scale, block_table=batch.block_tables)
+    last = torch.tensor(wl.cu_seqlens_q[1:] - 1, dtype=torch.int64, device=dev)
+    q_last = batch.q[last].contiguous()
+    lens_t = torch.tensor(lens, dtype=torch.int32, device=dev)
+    dec = pa.pa_decode(q_last, batch.k_cache, batch.v_cache, batch.block_tables, lens_t, scale, max(lens))
+    torch.cuda.synchronize()
+    # both are within tolerance of the same oracle rows; they use different arithmetic (MFMA vs dot2)
+    ref = oracle.prefill_varlen(tensors.to_u16(batch.q), tensors.to_u16(batch.k_new), tensors.to_u16(batch.v_new),
+                                wl.cu_seqlens_q, wl.cu_seqlens_k, scale)[wl.cu_seqlens_q[1:] - 1]
+    assert_attention_close(out[last], ref, "prefill last rows")
+    assert_attention_close(dec, ref, "decode of the same rows")
