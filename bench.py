@@ -92,7 +92,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--partition", type=int, default=0, help="decode split-K partition (0 = library choice)")
+    ap.add_argument("--split-waves", type=int, default=0, help="decode work split (0 = library choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -114,7 +114,7 @@ def main():
     b2 = tensors.materialize(wl2, dev)
     b3 = tensors.materialize(wl3, dev)
     b4 = tensors.materialize(wl4, dev)
-    ws_bytes = pa.pa_decode_workspace_size(wl2.num_seqs, 16, 8, 128, wl2.max_context_len, args.partition)
+    ws_bytes = pa.pa_decode_workspace_size(wl2.num_seqs, 16, 8, 128, wl2.max_context_len, args.split_waves)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     out2 = torch.empty((wl2.num_seqs, 16, 128), dtype=torch.bfloat16, device=dev)
     out3 = torch.empty((wl3.num_tokens, 16, 128), dtype=torch.bfloat16, device=dev)
@@ -125,7 +125,7 @@ def main():
     calls = {
         "store_decode": lambda: pa.pa_store_kvcache(b2.k_new, b2.v_new, b2.k_cache, b2.v_cache, b2.slot_mapping),
         "decode": lambda: pa.pa_decode(b2.q, b2.k_cache, b2.v_cache, b2.block_tables, b2.context_lens, scale, mk2,
-                                       out=out2, workspace=ws, partition_tokens=args.partition),
+                                       out=out2, workspace=ws, split_waves=args.split_waves),
         "store_prefill": lambda: pa.pa_store_kvcache(b3.k_new, b3.v_new, b3.k_cache, b3.v_cache, b3.slot_mapping),
         "prefill": lambda: pa.pa_prefill_varlen(b3.q, b3.k_new, b3.v_new, b3.cu_seqlens_q, b3.cu_seqlens_k, mq3,
                                                 scale, out=out3),
@@ -185,11 +185,11 @@ def main():
                         "4096-block pool) + varlen causal prefill (%d seqs, %d tokens) + prefix-cached prefill "
                         "(32 seqs, 1024 shared + %d new tokens)" % (wl3.num_seqs, wl3.num_tokens, wl4.num_tokens),
             "decode_kv_bytes": dbytes["kv"],
-            "decode_partition_tokens": pa.pa_decode_partition_tokens(wl2.num_seqs, 8, mk2, args.partition),
+            "decode_split_waves": pa.pa_decode_split_waves(wl2.num_seqs, 16, 8, mk2, args.split_waves),
             "prefill_flops": f3,
             "prefix_prefill_flops": f4,
         },
-        "roofline": {"bound": "hbm", "kernel": "pa_decode (partition + reduce kernels)",
+        "roofline": {"bound": "hbm", "kernel": "pa_decode (split + finalize kernels)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "bytes_per_launch": dbytes["total"], "avg_launch_us": round(ms["decode"] * 1e3, 2)},

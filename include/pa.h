@@ -93,16 +93,17 @@ int pa_store_kvcache(const void* k, int64_t k_token_stride, const void* v, int64
 /*
  * pa_decode_workspace_size — bytes of device workspace pa_decode needs.
  *
- * Host-only and pure. partition_tokens is the split-K partition length
- * (0 = the library's choice, else a positive multiple of 256). The same
- * arguments must be passed to pa_decode. Returns 0 for invalid arguments.
+ * Host-only and pure. split_waves is the number of waves the decode work is
+ * split over (0 = the library's choice, 2048, sized for the 256 CUs of an
+ * MI355X; fewer when there is less work). The same arguments must be passed
+ * to pa_decode. Returns 0 for invalid arguments.
  */
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                                int32_t max_context_len, int32_t partition_tokens);
+                                int32_t max_context_len, int32_t split_waves);
 
-/* Partition length pa_decode uses for these arguments (0 if invalid). */
-int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
-                                   int32_t partition_tokens);
+/* Number of waves pa_decode splits the work over for these arguments (0 if invalid). */
+int32_t pa_decode_split_waves(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t max_context_len,
+                              int32_t split_waves);
 
 /*
  * pa_decode — paged GQA decode attention.
@@ -118,22 +119,29 @@ int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_kv_heads, int32
  * Arithmetic: bf16 inputs, fp32 accumulation and softmax, bf16 output
  * (round to nearest even).
  *
+ * Work split: the (sequence, kv head) pairs are cut into chunks of 32 tokens
+ * (16 when G >= 4) and the chunk sequence is shared equally among
+ * split_waves waves; a pair cut by a share boundary is finished by a second,
+ * small kernel from fp32 partials (max, sum, unnormalised output) in the
+ * workspace (the split-K partition-and-reduce).
+ *
  * out           [num_seqs, num_q_heads, head_dim] bf16, contiguous.
  * q             [num_seqs, num_q_heads, head_dim] bf16; heads x dims
  *               contiguous, rows q_seq_stride elements apart.
  * k_cache, v_cache  as in pa_store_kvcache.
  * block_tables  [num_seqs, max_blocks_per_seq] int32; entries past
  *               ceil(L / block_size) are never read.
- * context_lens  [num_seqs] int32, each in [0, max_context_len].
+ * context_lens  [num_seqs] int32, each in [0, max_context_len];
+ *               max_context_len <= 2^24.
  * scale         softmax scale (1/sqrt(head_dim) for the pages' models).
- * workspace     device buffer of at least pa_decode_workspace_size(...) bytes
- *               (may be NULL when that size is 0); contents undefined after
- *               the call; must not be shared by work running concurrently.
+ * workspace     device buffer of at least pa_decode_workspace_size(...) bytes,
+ *               16-byte aligned; contents undefined after the call; must not
+ *               be shared by work running concurrently.
  */
 int pa_decode(void* out, const void* q, int64_t q_seq_stride, const void* k_cache, const void* v_cache,
               const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-              int32_t max_context_len, float scale, int32_t partition_tokens, void* workspace,
+              int32_t max_context_len, float scale, int32_t split_waves, void* workspace,
               size_t workspace_bytes, void* stream);
 
 /*

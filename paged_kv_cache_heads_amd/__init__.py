@@ -17,7 +17,7 @@ from ._lib import LibraryMissing  # noqa: F401
 
 __all__ = [
     "PAError", "LibraryMissing", "pa_store_kvcache", "pa_decode", "pa_decode_workspace_size",
-    "pa_decode_partition_tokens", "pa_prefill_varlen", "pa_status_string", "pa_last_error", "pa_version",
+    "pa_decode_split_waves", "pa_prefill_varlen", "pa_status_string", "pa_last_error", "pa_version",
     "library_path",
 ]
 
@@ -79,17 +79,18 @@ def pa_store_kvcache(k, v, k_cache, v_cache, slot_mapping, stream=None) -> None:
 
 
 def pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
-                             partition_tokens=0) -> int:
+                             split_waves=0) -> int:
     return int(_lib.load().pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
-                                                    max_context_len, partition_tokens))
+                                                    max_context_len, split_waves))
 
 
-def pa_decode_partition_tokens(num_seqs, num_kv_heads, max_context_len, partition_tokens=0) -> int:
-    return int(_lib.load().pa_decode_partition_tokens(num_seqs, num_kv_heads, max_context_len, partition_tokens))
+def pa_decode_split_waves(num_seqs, num_q_heads, num_kv_heads, max_context_len, split_waves=0) -> int:
+    return int(_lib.load().pa_decode_split_waves(num_seqs, num_q_heads, num_kv_heads, max_context_len,
+                                                 split_waves))
 
 
 def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, max_context_len: int, out=None,
-              workspace=None, partition_tokens: int = 0, stream=None):
+              workspace=None, split_waves: int = 0, stream=None):
     """Paged decode: q [B, Hq, D] bf16 -> out [B, Hq, D] bf16.
 
     workspace: a uint8 device tensor of at least pa_decode_workspace_size(...)
@@ -100,14 +101,14 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, max
     nb, bs, hkv, _ = k_cache.shape
     if out is None:
         out = torch.empty((b, hq, d), dtype=torch.bfloat16, device=q.device)
-    need = lib.pa_decode_workspace_size(b, hq, hkv, d, max_context_len, partition_tokens)
+    need = lib.pa_decode_workspace_size(b, hq, hkv, d, max_context_len, split_waves)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("pa_decode", lib.pa_decode(
         _ptr(out), _ptr(q), _rows(q, "q"), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
         int(block_tables.shape[1]), _ptr(context_lens), b, hq, hkv, d, bs, int(max_context_len), float(scale),
-        int(partition_tokens), _ptr(workspace), ws_bytes, _stream(stream, q.device)))
+        int(split_waves), _ptr(workspace), ws_bytes, _stream(stream, q.device)))
     return out
 
 

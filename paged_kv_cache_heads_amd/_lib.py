@@ -17,7 +17,7 @@ SIGNATURES = {
     "pa_version": (ctypes.c_int, []),
     "pa_store_kvcache": (ctypes.c_int, [_vp, _i64, _vp, _i64, _vp, _vp, _i32p, _i32, _i32, _i32, _i64, _i32, _vp]),
     "pa_decode_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
-    "pa_decode_partition_tokens": (_i32, [_i32, _i32, _i32, _i32]),
+    "pa_decode_split_waves": (_i32, [_i32, _i32, _i32, _i32, _i32]),
     "pa_decode": (ctypes.c_int, [_vp, _vp, _i64, _vp, _vp, _i32p, _i32, _i32p, _i32, _i32, _i32, _i32, _i32, _i32,
                                  _f32, _i32, _vp, _sz, _vp]),
     "pa_prefill_varlen": (ctypes.c_int, [_vp, _vp, _i64, _vp, _vp, _i64, _i64, _i32p, _i32p, _i32, _i32, _i32, _i32,

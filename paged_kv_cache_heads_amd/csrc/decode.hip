@@ -10,23 +10,34 @@
 // over the paged KV cache; section 3 "块管理器": fixed-size blocks).
 //
 // Design for gfx950 (HBM-bound, no MFMA):
-// * One workgroup (4 waves) per (partition of `partition` tokens, kv head,
-//   sequence). All G query heads of the kv head share each K/V row read.
-// * A wave takes 64 tokens at a time. Lane (r = lane / 8, s = lane % 8) loads
-//   16 bytes at d = 8s and 16 bytes at d = 64 + 8s of tokens i*8 + r
-//   (i = 0..7), so each load instruction reads eight whole 128-byte lines.
+// * Work is split stream-K style. The (sequence, kv head) pairs are laid end
+//   to end as runs of chunks of 8*TPL tokens, and each of `num_waves`
+//   one-wave workgroups takes an equal share of that chunk sequence, so all
+//   waves finish together whatever the mix of context lengths. Every wave
+//   derives its share from context_lens itself (a wave-wide scan); nothing is
+//   read back to the host.
+// * All G query heads of a kv head share each K/V row read. Lane
+//   (r = lane / 8, s = lane % 8) loads 16 bytes at d = 8s and 16 bytes at
+//   d = 64 + 8s of tokens i*8 + r (i < TPL): each load instruction reads eight
+//   whole 128-byte lines. The next chunk (possibly of the next pair) is loaded
+//   into a second register set while the current one is computed.
 // * q.k uses v_dot2_f32_bf16 on the raw bf16 pairs (fp32 accumulate); the
-//   8 partial dots per token are combined with a DPP reduce-scatter, after
-//   which lane (r, s) holds the score of token s*8 + r.
-// * Online softmax state (max, sum) is kept per 8-lane group, so the only
-//   per-chunk exchange is a 3-step DPP max; the group's p values are
-//   broadcast with ds_bpermute for the p.v update.
+//   per-lane partial dots are combined with a DPP reduce-scatter inside each
+//   8-lane group.
+// * Online-softmax state (max, sum) lives per 8-lane group, so the only
+//   per-chunk exchange is a 3-step DPP max; p values reach the lanes that
+//   hold the matching V rows with ds_bpermute. The accumulator rescale is
+//   skipped when no group's maximum moved.
 // * Masked positions (past the context) are *selected* to -inf and their rows
 //   are read from a clamped, valid address, so stale bits in the tail of the
 //   last block can never reach the output.
-// * A sequence that fits in one partition is normalised and written directly;
-//   longer ones write fp32 partials (o, max, sum) that decode_reduce_kernel
-//   combines: M = max_p m_p, o = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p.
+// * When a wave finishes a pair it merges its 8 groups with shuffles. A pair
+//   that lies wholly inside one wave's share is normalised and written
+//   directly. A pair cut by a share boundary leaves fp32 partials (o, max,
+//   sum) in the wave's two workspace slots (slot 0: a piece that continues a
+//   pair begun by an earlier wave; slot 1: a piece that starts a pair and
+//   is continued by later waves); decode_finalize_kernel combines them:
+//   M = max m_i, o = sum 2^(m_i - M) o_i / sum 2^(m_i - M) l_i.
 #include <math.h>
 
 #include "common.h"
@@ -35,152 +46,259 @@
 namespace pa {
 
 constexpr int kD = 128;
-constexpr int kDecodeThreads = 256;
-constexpr int kDecodeWaves = 4;
-constexpr int kChunk = 64;
+// Sum of TPL values (tokens i*8 + r, i < TPL) over the 8 lanes of group r.
+// On return every lane holds the group sum for token index s / (8 / TPL);
+// the 8 / TPL lanes sharing that index hold the same value.
+template <int TPL>
+__device__ __forceinline__ float group8_reduce(const float (&v)[TPL], int s) {
+  if constexpr (TPL == 4) {
+    const bool b2 = s & 4, b1 = s & 2;
+    float a[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const float send = b2 ? v[m] : v[m + 2];
+      const float keep = b2 ? v[m + 2] : v[m];
+      a[m] = keep + dpp<kDppHalfMirror>(send);
+    }
+    float c = (b1 ? a[1] : a[0]) + dpp<kDppXor2>(b1 ? a[0] : a[1]);
+    return c + dpp<kDppXor1>(c);
+  } else {
+    static_assert(TPL == 2, "2 or 4 tokens per lane");
+    const bool b2 = s & 4;
+    float c = (b2 ? v[1] : v[0]) + dpp<kDppHalfMirror>(b2 ? v[0] : v[1]);
+    c += dpp<kDppXor2>(c);
+    return c + dpp<kDppXor1>(c);
+  }
+}
+
+template <int TPL>
+struct ChunkRegs {
+  uint4 k[TPL][2];
+  uint4 v[TPL][2];
+};
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+struct Pos {
+  int b, g, k;  // sequence, kv head, chunk within the pair (wave-uniform)
+  int len, nc;  // context length and chunk count of sequence b
+};
+
+// Load the K and V rows of chunk p. Lane (r, s) reads tokens i*8 + r at byte
+// lane_off = r * row_bytes + 16 * s from the chunk's first row (uniform
+// base), so addresses are a scalar base plus a 32-bit lane offset. Only a
+// chunk running past the context end clamps its rows (to the last token).
+template <int TPL>
+__device__ __forceinline__ void load_chunk(ChunkRegs<TPL>& c, const DecodeArgs& a, const Pos& p, uint32_t row_bytes,
+                                           uint32_t lane_off, int r, int s) {
+  constexpr int CH = 8 * TPL;
+  const int bs = a.block_size;
+  const int tok0 = p.k * CH;
+  // block_size is a multiple of 64 and tok0 a multiple of the chunk: one block per chunk
+  const int blk = a.block_tables[(int64_t)p.b * a.max_blocks_per_seq + tok0 / bs];
+  const int64_t base = ((int64_t)blk * bs + tok0 % bs) * a.num_kv_heads * kD + p.g * kD;
+  const char* kb = reinterpret_cast<const char*>(a.k_cache + base);
+  const char* vb = reinterpret_cast<const char*>(a.v_cache + base);
+  const int nvalid = p.len - tok0;
+  if (nvalid >= CH) {
+#pragma unroll
+    for (int i = 0; i < TPL; ++i) {
+      const uint32_t off = lane_off + i * 8 * row_bytes;
+      c.k[i][0] = load16_nt(kb + off);
+      c.k[i][1] = load16_nt(kb + off + 128);
+    }
+#pragma unroll
+    for (int i = 0; i < TPL; ++i) {
+      const uint32_t off = lane_off + i * 8 * row_bytes;
+      c.v[i][0] = load16_nt(vb + off);
+      c.v[i][1] = load16_nt(vb + off + 128);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < TPL; ++i) {
+      const uint32_t off = (uint32_t)min(i * 8 + r, nvalid - 1) * row_bytes + 16 * s;
+      c.k[i][0] = load16_nt(kb + off);
+      c.k[i][1] = load16_nt(kb + off + 128);
+    }
+#pragma unroll
+    for (int i = 0; i < TPL; ++i) {
+      const uint32_t off = (uint32_t)min(i * 8 + r, nvalid - 1) * row_bytes + 16 * s;
+      c.v[i][0] = load16_nt(vb + off);
+      c.v[i][1] = load16_nt(vb + off + 128);
+    }
+  }
+}
 
 template <int G>
-__global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(DecodeArgs a) {
-  __shared__ float red_o[kDecodeWaves][G][kD];
-  __shared__ float red_m[G][kDecodeWaves * 8];
-  __shared__ float red_l[G][kDecodeWaves * 8];
-
-  const int part = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-  const int L = a.context_lens[b];
-  const int start = part * a.partition;
-  const int tid = threadIdx.x;
-  if (start >= L) {
-    if (L <= 0 && part == 0) {
-      // Empty context: the output rows are zero.
-      uint32_t* o = reinterpret_cast<uint32_t*>(a.out + ((int64_t)b * a.num_q_heads + kvh * G) * kD);
-      for (int i = tid; i < G * kD / 2; i += kDecodeThreads) o[i] = 0u;
-    }
-    return;
-  }
-  const int end = min(start + a.partition, L);
-  const int wave = tid >> 6, lane = tid & 63, r = lane >> 3, s = lane & 7;
-  const int64_t row = (int64_t)a.num_kv_heads * kD;
-  const int bs = a.block_size;
-
-  uint4 qlo[G], qhi[G];
-#pragma unroll
-  for (int j = 0; j < G; ++j) {
-    const bf16_t* qp = a.q + (int64_t)b * a.q_seq_stride + (int64_t)(kvh * G + j) * kD;
-    qlo[j] = load16(qp + 8 * s);
-    qhi[j] = load16(qp + 64 + 8 * s);
-  }
-
+struct DecodeState {
   float m[G], l[G], acc[G][16];
+};
+
+template <int G>
+struct QRegs {
+  uint4 lo[G], hi[G];
+};
+
+template <int G, int TPL>
+__device__ __forceinline__ void compute_chunk(DecodeState<G>& st, const QRegs<G>& q, const ChunkRegs<TPL>& c,
+                                              int nvalid, float scale_log2e, int lane, int r, int s) {
+  constexpr int kDup = 8 / TPL;  // lanes holding each token's score
+  const bool valid = ((s / kDup) * 8 + r) < nvalid;
+  float pb[G][TPL];
 #pragma unroll
   for (int j = 0; j < G; ++j) {
-    m[j] = kNegBig;
-    l[j] = 0.f;
+    float sc[TPL];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) acc[j][e] = 0.f;
+    for (int i = 0; i < TPL; ++i) {
+      float d = 0.f;
+      d = dot2_bf16(q.lo[j].x, c.k[i][0].x, d);
+      d = dot2_bf16(q.lo[j].y, c.k[i][0].y, d);
+      d = dot2_bf16(q.lo[j].z, c.k[i][0].z, d);
+      d = dot2_bf16(q.lo[j].w, c.k[i][0].w, d);
+      d = dot2_bf16(q.hi[j].x, c.k[i][1].x, d);
+      d = dot2_bf16(q.hi[j].y, c.k[i][1].y, d);
+      d = dot2_bf16(q.hi[j].z, c.k[i][1].z, d);
+      d = dot2_bf16(q.hi[j].w, c.k[i][1].w, d);
+      sc[i] = d;
+    }
+    float x = group8_reduce<TPL>(sc, s);  // score of token (s / kDup) * 8 + r
+    x = valid ? x * scale_log2e : -INFINITY;
+    const float mnew = fmaxf(st.m[j], group8_max(x));
+    const float p = exp2f(x - mnew);
+    if (__ballot(mnew != st.m[j])) {
+      const float alpha = exp2f(st.m[j] - mnew);
+      st.l[j] *= alpha;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) st.acc[j][e] *= alpha;
+    }
+    st.m[j] = mnew;
+    st.l[j] += (s % kDup) ? 0.f : p;  // count each token once
+#pragma unroll
+    for (int i = 0; i < TPL; ++i) pb[j][i] = __shfl(p, (lane & ~7) | (kDup * i));
   }
-
-  const float c = a.scale_log2e;
-  const int32_t* table = a.block_tables + (int64_t)b * a.max_blocks_per_seq;
-
-  for (int cb = start + wave * kChunk; cb < end; cb += kDecodeWaves * kChunk) {
-    const int nvalid = end - cb;  // >= 1
-    // block_size is a multiple of 64 and cb a multiple of 64: one block per chunk
-    const int blk = table[cb / bs];
-    const int64_t base = ((int64_t)blk * bs + (cb % bs)) * row + kvh * kD;
-    const bf16_t* kb = a.k_cache + base;
-    const bf16_t* vb = a.v_cache + base;
-    uint4 kl[8], kh[8], vl[8], vh[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int t = min(i * 8 + r, nvalid - 1);
-      const int64_t off = (int64_t)t * row;
-      kl[i] = load16(kb + off + 8 * s);
-      kh[i] = load16(kb + off + 64 + 8 * s);
-    }
+  for (int i = 0; i < TPL; ++i) {
+    float vv[16];
+    vv[0] = bf16_lo(c.v[i][0].x); vv[1] = bf16_hi(c.v[i][0].x);
+    vv[2] = bf16_lo(c.v[i][0].y); vv[3] = bf16_hi(c.v[i][0].y);
+    vv[4] = bf16_lo(c.v[i][0].z); vv[5] = bf16_hi(c.v[i][0].z);
+    vv[6] = bf16_lo(c.v[i][0].w); vv[7] = bf16_hi(c.v[i][0].w);
+    vv[8] = bf16_lo(c.v[i][1].x); vv[9] = bf16_hi(c.v[i][1].x);
+    vv[10] = bf16_lo(c.v[i][1].y); vv[11] = bf16_hi(c.v[i][1].y);
+    vv[12] = bf16_lo(c.v[i][1].z); vv[13] = bf16_hi(c.v[i][1].z);
+    vv[14] = bf16_lo(c.v[i][1].w); vv[15] = bf16_hi(c.v[i][1].w);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int t = min(i * 8 + r, nvalid - 1);
-      const int64_t off = (int64_t)t * row;
-      vl[i] = load16(vb + off + 8 * s);
-      vh[i] = load16(vb + off + 64 + 8 * s);
-    }
-
-    const bool valid = (s * 8 + r) < nvalid;
-    float pb[G][8];
+    for (int j = 0; j < G; ++j)
 #pragma unroll
-    for (int j = 0; j < G; ++j) {
-      float sc[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        float d = 0.f;
-        d = dot2_bf16(qlo[j].x, kl[i].x, d);
-        d = dot2_bf16(qlo[j].y, kl[i].y, d);
-        d = dot2_bf16(qlo[j].z, kl[i].z, d);
-        d = dot2_bf16(qlo[j].w, kl[i].w, d);
-        d = dot2_bf16(qhi[j].x, kh[i].x, d);
-        d = dot2_bf16(qhi[j].y, kh[i].y, d);
-        d = dot2_bf16(qhi[j].z, kh[i].z, d);
-        d = dot2_bf16(qhi[j].w, kh[i].w, d);
-        sc[i] = d;
-      }
-      float x = group8_reduce_scatter(sc, s);  // score of token s*8 + r
-      x = valid ? x * c : -INFINITY;
-      const float mnew = fmaxf(m[j], group8_max(x));
-      const float alpha = exp2f(m[j] - mnew);
-      const float p = exp2f(x - mnew);
-      l[j] = l[j] * alpha + p;
-      m[j] = mnew;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[j][e] *= alpha;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) pb[j][i] = __shfl(p, (lane & ~7) | i);
-    }
-
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float vv[16];
-      vv[0] = bf16_lo(vl[i].x); vv[1] = bf16_hi(vl[i].x);
-      vv[2] = bf16_lo(vl[i].y); vv[3] = bf16_hi(vl[i].y);
-      vv[4] = bf16_lo(vl[i].z); vv[5] = bf16_hi(vl[i].z);
-      vv[6] = bf16_lo(vl[i].w); vv[7] = bf16_hi(vl[i].w);
-      vv[8] = bf16_lo(vh[i].x); vv[9] = bf16_hi(vh[i].x);
-      vv[10] = bf16_lo(vh[i].y); vv[11] = bf16_hi(vh[i].y);
-      vv[12] = bf16_lo(vh[i].z); vv[13] = bf16_hi(vh[i].z);
-      vv[14] = bf16_lo(vh[i].w); vv[15] = bf16_hi(vh[i].w);
-#pragma unroll
-      for (int j = 0; j < G; ++j)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[j][e] = fmaf(pb[j][i], vv[e], acc[j][e]);
-    }
+      for (int e = 0; e < 16; ++e) st.acc[j][e] = fmaf(pb[j][i], vv[e], st.acc[j][e]);
   }
+}
 
-  // ---- merge the 32 groups (8 per wave x 4 waves) of this workgroup ----
+// ---- wave-wide helpers for the work split ----
+__device__ __forceinline__ int wave_sum_i32(int x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
+__device__ __forceinline__ int wave_inclusive_scan_i32(int x, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+__device__ __forceinline__ int chunks_of(int len, int ch) { return len > 0 ? (len + ch - 1) / ch : 0; }
+
+// Chunks per kv head summed over sequences [0, upto) (wave-uniform result).
+// Each lane takes 4 consecutive sequences of a 256-sequence tile, so one
+// round of loads covers up to 256 sequences.
+__device__ __forceinline__ int64_t chunk_prefix(const int32_t* lens, int upto, int ch, int lane) {
+  int64_t run = 0;
+  for (int base = 0; base < upto; base += 256) {
+    int x = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int b = base + lane * 4 + u;
+      x += b < upto ? chunks_of(lens[b], ch) : 0;
+    }
+    run += __builtin_amdgcn_readfirstlane(wave_sum_i32(x));
+  }
+  return run;
+}
+
+// First chunk index of wave w's share: floor(w * C / NW).
+__device__ __forceinline__ int64_t share_begin(int64_t w, int64_t total, int64_t nw) { return w * total / nw; }
+
+// The wave whose share holds chunk c: the largest w with share_begin(w) <= c.
+__device__ __forceinline__ int64_t wave_of_chunk(int64_t c, int64_t total, int64_t nw) {
+  return ((c + 1) * nw + total - 1) / total - 1;
+}
+
+template <int G>
+__device__ __forceinline__ void load_q(QRegs<G>& q, const DecodeArgs& a, int b, int g, int s) {
 #pragma unroll
   for (int j = 0; j < G; ++j) {
-    const float lg = group8_sum(l[j]);
-    if (s == 0) {
-      red_m[j][wave * 8 + r] = m[j];
-      red_l[j][wave * 8 + r] = lg;
-    }
+    const bf16_t* qp = a.q + (int64_t)b * a.q_seq_stride + (int64_t)(g * G + j) * kD;
+    q.lo[j] = load16(qp + 8 * s);
+    q.hi[j] = load16(qp + 64 + 8 * s);
   }
-  __syncthreads();
+}
+
+// Next chunk in (sequence, kv head, chunk) order; skips empty sequences.
+__device__ __forceinline__ Pos next_pos(const Pos& p, const DecodeArgs& a, int ch) {
+  if (p.k + 1 < p.nc) return Pos{p.b, p.g, p.k + 1, p.len, p.nc};
+  if (p.g + 1 < a.num_kv_heads) return Pos{p.b, p.g + 1, 0, p.len, p.nc};
+  Pos n{p.b + 1, 0, 0, 0, 0};
+  for (; n.b < a.num_seqs; ++n.b) {
+    n.len = uniform(a.context_lens[n.b]);
+    n.nc = chunks_of(n.len, ch);
+    if (n.nc > 0) break;
+  }
+  return n;
+}
+
+template <int G>
+__device__ __forceinline__ void reset_state(DecodeState<G>& st) {
 #pragma unroll
   for (int j = 0; j < G; ++j) {
-    float M = kNegBig;
+    st.m[j] = kNegBig;
+    st.l[j] = 0.f;
 #pragma unroll
-    for (int k = 0; k < kDecodeWaves * 8; ++k) M = fmaxf(M, red_m[j][k]);
-    const float f = exp2f(m[j] - M);
-    float v16[16];
+    for (int e = 0; e < 16; ++e) st.acc[j][e] = 0.f;
+  }
+}
+
+// Merge the wave's 8 groups for the piece of pair (p.b, p.g) that ends at
+// chunk p.k, and write it: final output if the piece is the whole pair, else
+// a partial into the wave's slot.
+template <int G>
+__device__ __forceinline__ void finish_piece(const DecodeState<G>& st, const DecodeArgs& a, const Pos& p, int k0,
+                                             int wave, int lane, int s) {
+  const bool whole = (k0 == 0) && (p.k == p.nc - 1);
+  const int64_t slot = (int64_t)wave * 2 + (k0 > 0 ? 0 : 1);
+  const bool h3 = lane & 8, h4 = lane & 16, h5 = lane & 32;
+  const int e0 = (h3 ? 8 : 0) + (h4 ? 4 : 0) + (h5 ? 2 : 0);
+  const int d = e0 < 8 ? 8 * s + e0 : 64 + 8 * s + (e0 - 8);  // this lane's output pair: d, d + 1
 #pragma unroll
-    for (int e = 0; e < 16; ++e) v16[e] = acc[j][e] * f;
-    // reduce-scatter over r (lane bits 3, 4, 5)
-    const bool h3 = lane & 8, h4 = lane & 16, h5 = lane & 32;
+  for (int j = 0; j < G; ++j) {
+    float M = st.m[j];
+    M = fmaxf(M, dpp<kDppRor8>(M));
+    M = fmaxf(M, __shfl_xor(M, 16));
+    M = fmaxf(M, __shfl_xor(M, 32));
+    const float f = exp2f(st.m[j] - M);
+    float Ls = group8_sum(st.l[j]) * f;
+    Ls += dpp<kDppRor8>(Ls);
+    Ls += __shfl_xor(Ls, 16);
+    Ls += __shfl_xor(Ls, 32);
     float v8[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float send = h3 ? v16[e] : v16[e + 8];
-      const float keep = h3 ? v16[e + 8] : v16[e];
-      v8[e] = keep + __shfl_xor(send, 8);
+      const float send = (h3 ? st.acc[j][e] : st.acc[j][e + 8]) * f;
+      const float keep = (h3 ? st.acc[j][e + 8] : st.acc[j][e]) * f;
+      v8[e] = keep + dpp<kDppRor8>(send);
     }
     float v4[4];
 #pragma unroll
@@ -196,82 +314,205 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(Decode
       const float keep = h5 ? v4[e + 2] : v4[e];
       v2[e] = keep + __shfl_xor(send, 32);
     }
-    const int e0 = (h3 ? 8 : 0) + (h4 ? 4 : 0) + (h5 ? 2 : 0);
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int e = e0 + k;
-      const int d = e < 8 ? 8 * s + e : 64 + 8 * s + (e - 8);
-      red_o[wave][j][d] = v2[k];
-    }
-  }
-  __syncthreads();
-
-  const int nparts = (L + a.partition - 1) / a.partition;
-  for (int idx = tid; idx < G * kD / 2; idx += kDecodeThreads) {
-    const int j = idx / (kD / 2);
-    const int d = (idx % (kD / 2)) * 2;
-    float M = kNegBig;
-#pragma unroll
-    for (int k = 0; k < kDecodeWaves * 8; ++k) M = fmaxf(M, red_m[j][k]);
-    float Ls = 0.f;
-#pragma unroll
-    for (int k = 0; k < kDecodeWaves * 8; ++k) Ls += red_l[j][k] * exp2f(red_m[j][k] - M);
-    float o0 = 0.f, o1 = 0.f;
-#pragma unroll
-    for (int w = 0; w < kDecodeWaves; ++w) {
-      o0 += red_o[w][j][d];
-      o1 += red_o[w][j][d + 1];
-    }
-    const int h = kvh * G + j;
-    if (nparts == 1) {
+    if (whole) {
       const float inv = 1.f / Ls;
-      reinterpret_cast<uint32_t*>(a.out + ((int64_t)b * a.num_q_heads + h) * kD)[d / 2] =
-          pack_bf16x2(o0 * inv, o1 * inv);
+      const int h = p.g * G + j;
+      reinterpret_cast<uint32_t*>(a.out + ((int64_t)p.b * a.num_q_heads + h) * kD)[d / 2] =
+          pack_bf16x2(v2[0] * inv, v2[1] * inv);
     } else {
-      const int64_t slot = ((int64_t)b * a.num_q_heads + h) * a.num_partitions + part;
-      reinterpret_cast<float2*>(a.ws_o + slot * kD)[d / 2] = make_float2(o0, o1);
-      if (d == 0) reinterpret_cast<float2*>(a.ws_ml)[slot] = make_float2(M, Ls);
+      reinterpret_cast<float2*>(a.ws_o + (slot * G + j) * kD)[d / 2] = make_float2(v2[0], v2[1]);
+      if (lane == 0) reinterpret_cast<float2*>(a.ws_ml)[slot * G + j] = make_float2(M, Ls);
     }
   }
 }
 
-// One wave per (sequence, query head) with more than one partition.
-__global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int h = blockIdx.x * 4 + wave;
-  const int b = blockIdx.y;
-  if (h >= a.num_q_heads) return;
-  const int L = a.context_lens[b];
-  const int np = (L + a.partition - 1) / a.partition;
-  if (np <= 1) return;
-  const int64_t slot0 = ((int64_t)b * a.num_q_heads + h) * a.num_partitions;
-  const float2* ml = reinterpret_cast<const float2*>(a.ws_ml) + slot0;
-  const float* o = a.ws_o + slot0 * kD;
-  float M = kNegBig;
-  for (int p = 0; p < np; ++p) M = fmaxf(M, ml[p].x);
-  float Ls = 0.f, o0 = 0.f, o1 = 0.f;
-  for (int p = 0; p < np; ++p) {
-    const float2 st = ml[p];
-    const float w = exp2f(st.x - M);
-    Ls += w * st.y;
-    const float2 ov = reinterpret_cast<const float2*>(o + (int64_t)p * kD)[lane];
-    o0 += w * ov.x;
-    o1 += w * ov.y;
+template <int G, int TPL>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(G >= 8 ? 1 : 2, 8))) void decode_split_kernel(DecodeArgs a) {
+  constexpr int CH = 8 * TPL;  // tokens per chunk
+  const int wave = blockIdx.x, lane = threadIdx.x;
+  const int r = lane >> 3, s = lane & 7;
+  const int64_t nw = a.num_waves;
+  const int64_t total = chunk_prefix(a.context_lens, a.num_seqs, CH, lane) * a.num_kv_heads;
+  const int64_t lo = share_begin(wave, total, nw), hi = share_begin(wave + 1, total, nw);
+  if (lo >= hi) return;
+
+  // locate chunk `lo`: the sequence b with kvh*prefix(b) <= lo < kvh*prefix(b+1)
+  Pos cur{0, 0, 0, 0, 0};
+  {
+    int64_t run = 0;
+    for (int base = 0; base < a.num_seqs; base += 256) {
+      int len[4], x[4], sum = 0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int b = base + lane * 4 + u;
+        len[u] = b < a.num_seqs ? a.context_lens[b] : 0;
+        x[u] = chunks_of(len[u], CH) * a.num_kv_heads;
+        sum += x[u];
+      }
+      const int incl = wave_inclusive_scan_i32(sum, lane);
+      const int64_t lane_beg = run + incl - sum;
+      const uint64_t hit = __ballot(sum > 0 && lane_beg <= lo && lo < run + incl);
+      if (hit) {
+        const int src = __ffsll((unsigned long long)hit) - 1;
+        // walk the 4 sequences of lane src
+        int64_t beg = uniform(__shfl((int)(lane_beg - run), src)) + run;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int xu = uniform(__shfl(x[u], src));
+          if (xu > 0 && lo < beg + xu && cur.nc == 0) {
+            cur.b = base + src * 4 + u;
+            cur.len = uniform(__shfl(len[u], src));
+            cur.nc = chunks_of(cur.len, CH);
+            const int64_t rel = lo - beg;
+            cur.g = (int)(rel / cur.nc);
+            cur.k = (int)(rel % cur.nc);
+          }
+          beg += xu;
+        }
+        break;
+      }
+      run += uniform(__shfl(incl, 63));
+    }
   }
-  const float inv = 1.f / Ls;
-  reinterpret_cast<uint32_t*>(a.out + ((int64_t)b * a.num_q_heads + h) * kD)[lane] = pack_bf16x2(o0 * inv, o1 * inv);
+
+  const uint32_t row_bytes = (uint32_t)a.num_kv_heads * kD * 2;
+  const uint32_t lane_off = r * row_bytes + 16 * s;
+  ChunkRegs<TPL> c0, c1;
+  QRegs<G> q0, q1;
+  DecodeState<G> st;
+  load_chunk(c0, a, cur, row_bytes, lane_off, r, s);
+  load_q(q0, a, cur.b, cur.g, s);
+  reset_state(st);
+  int k0 = cur.k;  // first chunk of the current piece
+  const float sc = a.scale_log2e;
+
+  // Two stages with the register sets swapped (no copies between them).
+  for (int64_t c = lo;;) {
+    {
+      const bool more = c + 1 < hi;
+      Pos nxt = cur;
+      bool new_pair = false;
+      if (more) {
+        nxt = next_pos(cur, a, CH);
+        new_pair = nxt.b != cur.b || nxt.g != cur.g;
+        load_chunk(c1, a, nxt, row_bytes, lane_off, r, s);
+        if (new_pair) load_q(q1, a, nxt.b, nxt.g, s);
+      }
+      compute_chunk<G, TPL>(st, q0, c0, cur.len - cur.k * CH, sc, lane, r, s);
+      if (!more || new_pair) {
+        finish_piece<G>(st, a, cur, k0, wave, lane, s);
+        if (!more) break;
+        reset_state(st);
+        k0 = 0;
+        q0 = q1;
+      }
+      cur = nxt;
+      ++c;
+    }
+    {
+      const bool more = c + 1 < hi;
+      Pos nxt = cur;
+      bool new_pair = false;
+      if (more) {
+        nxt = next_pos(cur, a, CH);
+        new_pair = nxt.b != cur.b || nxt.g != cur.g;
+        load_chunk(c0, a, nxt, row_bytes, lane_off, r, s);
+        if (new_pair) load_q(q1, a, nxt.b, nxt.g, s);
+      }
+      compute_chunk<G, TPL>(st, q0, c1, cur.len - cur.k * CH, sc, lane, r, s);
+      if (!more || new_pair) {
+        finish_piece<G>(st, a, cur, k0, wave, lane, s);
+        if (!more) break;
+        reset_state(st);
+        k0 = 0;
+        q0 = q1;
+      }
+      cur = nxt;
+      ++c;
+    }
+  }
 }
 
+// One wave per (sequence, kv head): zero rows for an empty context, and for
+// a pair cut by share boundaries, combine the pieces its waves left in their
+// slots (slot 1 of the first wave, slot 0 of every later non-empty wave).
+template <int G, int TPL>
+__global__ __launch_bounds__(64) void decode_finalize_kernel(DecodeArgs a) {
+  constexpr int CH = 8 * TPL;
+  const int b = blockIdx.x / a.num_kv_heads, g = blockIdx.x % a.num_kv_heads, lane = threadIdx.x;
+  const int len = a.context_lens[b];
+  const int nc = chunks_of(len, CH);
+  if (nc == 0) {
+    uint32_t* o = reinterpret_cast<uint32_t*>(a.out + ((int64_t)b * a.num_q_heads + g * G) * kD);
+    for (int i = lane; i < G * kD / 2; i += 64) o[i] = 0u;
+    return;
+  }
+  const int64_t nw = a.num_waves;
+  const int64_t total = chunk_prefix(a.context_lens, a.num_seqs, CH, lane) * a.num_kv_heads;
+  const int64_t first = chunk_prefix(a.context_lens, b, CH, lane) * a.num_kv_heads + (int64_t)g * nc;
+  const int64_t w1 = wave_of_chunk(first, total, nw), w2 = wave_of_chunk(first + nc - 1, total, nw);
+  if (w1 == w2) return;  // written whole by its wave
+  float M[G], Ls[G], o0[G], o1[G];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    M[j] = kNegBig;
+    Ls[j] = 0.f;
+    o0[j] = o1[j] = 0.f;
+  }
+  // pieces in batches of 64, one lane per piece; online rescale across batches
+  for (int64_t wb = w1; wb <= w2; wb += 64) {
+    const int64_t w = wb + lane;
+    const bool live = w <= w2 && (w == w1 || share_begin(w, total, nw) < share_begin(w + 1, total, nw));
+    const int64_t slot = w * 2 + (w == w1 ? 1 : 0);
+    const int n = (int)min<int64_t>(64, w2 - wb + 1);
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const float2 ml = live ? reinterpret_cast<const float2*>(a.ws_ml)[slot * G + j] : make_float2(kNegBig, 0.f);
+      float mb = ml.x;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) mb = fmaxf(mb, __shfl_xor(mb, off));
+      const float mnew = fmaxf(M[j], mb);
+      const float alpha = exp2f(M[j] - mnew);
+      const float f = live ? exp2f(ml.x - mnew) : 0.f;
+      float lf = f * ml.y;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) lf += __shfl_xor(lf, off);
+      Ls[j] = Ls[j] * alpha + lf;
+      o0[j] *= alpha;
+      o1[j] *= alpha;
+      M[j] = mnew;
+      for (int i = 0; i < n; ++i) {
+        const float fi = __shfl(f, i);
+        const int64_t si = __shfl(slot, i);
+        if (fi != 0.f) {
+          const float2 ov = reinterpret_cast<const float2*>(a.ws_o + (si * G + j) * kD)[lane];
+          o0[j] += fi * ov.x;
+          o1[j] += fi * ov.y;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    const float inv = 1.f / Ls[j];
+    reinterpret_cast<uint32_t*>(a.out + ((int64_t)b * a.num_q_heads + g * G + j) * kD)[lane] =
+        pack_bf16x2(o0[j] * inv, o1[j] * inv);
+  }
+}
+
+// Tokens per lane per chunk: 4 while the G heads' state is small, else 2, so
+// that two waves fit per SIMD.
 template <int G>
 static hipError_t launch_decode_g(const DecodeArgs& a, hipStream_t stream) {
-  dim3 grid(a.num_partitions, a.num_kv_heads, a.num_seqs);
-  hipLaunchKernelGGL(decode_partition_kernel<G>, grid, dim3(kDecodeThreads), 0, stream, a);
+  constexpr int TPL = G <= 2 ? 4 : 2;
+  decode_split_kernel<G, TPL><<<dim3(a.num_waves), dim3(64), 0, stream>>>(a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.num_partitions <= 1) return e;
-  dim3 rgrid((a.num_q_heads + 3) / 4, a.num_seqs);
-  hipLaunchKernelGGL(decode_reduce_kernel, rgrid, dim3(256), 0, stream, a);
+  if (e != hipSuccess) return e;
+  decode_finalize_kernel<G, TPL><<<dim3(a.num_seqs * a.num_kv_heads), dim3(64), 0, stream>>>(a);
   return hipGetLastError();
 }
+
+int decode_chunk_tokens(int group) { return group <= 2 ? 32 : 16; }
 
 hipError_t launch_decode(const DecodeArgs& a, int group, hipStream_t stream) {
   if (a.num_seqs == 0) return hipSuccess;

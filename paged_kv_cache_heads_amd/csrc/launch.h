@@ -27,15 +27,14 @@ struct DecodeArgs {
   const uint16_t* v_cache;
   const int32_t* block_tables;
   const int32_t* context_lens;
-  float* ws_o;   // [num_seqs, num_q_heads, num_partitions, head_dim]
-  float* ws_ml;  // [num_seqs, num_q_heads, num_partitions, 2]  (max, sum)
+  float* ws_o;   // [num_waves * 2 slots, G, head_dim] partial outputs
+  float* ws_ml;  // [num_waves * 2 slots, G, 2] (max, sum) of each partial
   int32_t max_blocks_per_seq;
   int32_t num_seqs;
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t block_size;
-  int32_t partition;       // tokens per partition (multiple of 256)
-  int32_t num_partitions;  // ceil(max_context_len / partition)
+  int32_t num_waves;  // waves the chunk sequence is split over
   float scale_log2e;
 };
 
@@ -63,6 +62,8 @@ struct PrefillArgs {
 hipError_t launch_store_kvcache(const StoreArgs& a, hipStream_t stream);
 // group = num_q_heads / num_kv_heads (1, 2, 4 or 8); head_dim is 128.
 hipError_t launch_decode(const DecodeArgs& a, int group, hipStream_t stream);
+// Tokens per decode work chunk for a GQA group size.
+int decode_chunk_tokens(int group);
 hipError_t launch_prefill(const PrefillArgs& a, int group, hipStream_t stream);
 
 // Query positions covered by one prefill workgroup for a GQA group size.

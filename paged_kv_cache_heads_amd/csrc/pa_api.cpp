@@ -59,36 +59,29 @@ int hip_status(hipError_t e, const char* what) {
   return fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-// Split-K partition length (tokens). Chosen from sizes known on the host only.
-int32_t choose_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len, int32_t requested) {
-  if (requested > 0) return requested;
-  (void)num_seqs;
-  (void)num_kv_heads;
-  int32_t p = 512;
-  // keep the partition count per sequence at or below 64
-  while ((int64_t)p * 64 < (int64_t)max_context_len) p *= 2;
-  return p;
-}
+// Waves the decode work is split over: enough to keep every CU of an MI355X
+// (256 CUs, 8 resident decode waves each) busy, but no more than there are
+// chunks of work.
+constexpr int32_t kDecodeWaves = 2048;
 
 struct DecodeGeometry {
-  int32_t partition;
-  int32_t num_partitions;
+  int32_t num_waves;
   size_t ws_o_bytes;
   size_t ws_bytes;
 };
 
 bool decode_geometry(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t max_context_len,
-                     int32_t partition_tokens, DecodeGeometry* g) {
-  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_context_len < 0) return false;
-  if (partition_tokens < 0 || partition_tokens % 256 != 0) return false;
-  g->partition = choose_partition(num_seqs, num_kv_heads, max_context_len, partition_tokens);
-  g->num_partitions = max_context_len == 0 ? 1 : (max_context_len + g->partition - 1) / g->partition;
-  if (g->num_partitions <= 1) {
-    g->ws_o_bytes = 0;
-    g->ws_bytes = 0;
-    return true;
-  }
-  const size_t slots = (size_t)num_seqs * num_q_heads * g->num_partitions;
+                     int32_t split_waves, DecodeGeometry* g) {
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_context_len < 0 || split_waves < 0) return false;
+  if (num_q_heads % num_kv_heads != 0) return false;
+  const int group = num_q_heads / num_kv_heads;
+  const int ch = pa::decode_chunk_tokens(group);
+  const int64_t max_chunks = (int64_t)num_seqs * num_kv_heads * ((max_context_len + ch - 1) / ch);
+  int64_t nw = split_waves > 0 ? split_waves : kDecodeWaves;
+  if (nw > max_chunks) nw = max_chunks;
+  if (nw < 1) nw = 1;
+  g->num_waves = (int32_t)nw;
+  const size_t slots = (size_t)nw * 2 * group;
   g->ws_o_bytes = slots * kHeadDim * sizeof(float);
   g->ws_bytes = g->ws_o_bytes + slots * 2 * sizeof(float);
   return true;
@@ -155,38 +148,38 @@ int pa_store_kvcache(const void* k, int64_t k_token_stride, const void* v, int64
 }
 
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                                int32_t max_context_len, int32_t partition_tokens) {
+                                int32_t max_context_len, int32_t split_waves) {
   if (head_dim != kHeadDim) return 0;
   DecodeGeometry g;
-  if (!decode_geometry(num_seqs, num_q_heads, num_kv_heads, max_context_len, partition_tokens, &g)) return 0;
+  if (!decode_geometry(num_seqs, num_q_heads, num_kv_heads, max_context_len, split_waves, &g)) return 0;
   return g.ws_bytes;
 }
 
-int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
-                                   int32_t partition_tokens) {
+int32_t pa_decode_split_waves(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t max_context_len,
+                              int32_t split_waves) {
   DecodeGeometry g;
-  if (!decode_geometry(num_seqs, 1 * num_kv_heads, num_kv_heads, max_context_len, partition_tokens, &g)) return 0;
-  return g.partition;
+  if (!decode_geometry(num_seqs, num_q_heads, num_kv_heads, max_context_len, split_waves, &g)) return 0;
+  return g.num_waves;
 }
 
 int pa_decode(void* out, const void* q, int64_t q_seq_stride, const void* k_cache, const void* v_cache,
               const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-              int32_t max_context_len, float scale, int32_t partition_tokens, void* workspace,
+              int32_t max_context_len, float scale, int32_t split_waves, void* workspace,
               size_t workspace_bytes, void* stream) {
   if (num_seqs < 0) return fail(PA_ERR_INVALID_ARGUMENT, "num_seqs %d is negative", num_seqs);
   if (num_seqs > 65535) return fail(PA_ERR_UNSUPPORTED, "num_seqs %d exceeds 65535", num_seqs);
   int st = check_heads(num_q_heads, num_kv_heads, head_dim);
   if (st) return st;
+  if (max_context_len > (1 << 24))
+    return fail(PA_ERR_UNSUPPORTED, "max_context_len %d exceeds 2^24", max_context_len);
   st = check_block_size(block_size);
   if (st) return st;
   if (max_context_len < 0) return fail(PA_ERR_INVALID_ARGUMENT, "max_context_len %d is negative", max_context_len);
   if (max_blocks_per_seq < 0 || (int64_t)max_blocks_per_seq * block_size < max_context_len)
     return fail(PA_ERR_INVALID_ARGUMENT, "max_blocks_per_seq (%d) x block_size (%d) < max_context_len (%d)",
                 max_blocks_per_seq, block_size, max_context_len);
-  if (partition_tokens < 0 || partition_tokens % 256 != 0)
-    return fail(PA_ERR_INVALID_ARGUMENT, "partition_tokens %d must be 0 or a positive multiple of 256",
-                partition_tokens);
+  if (split_waves < 0) return fail(PA_ERR_INVALID_ARGUMENT, "split_waves %d is negative", split_waves);
   if (!(scale == scale) || isinf(scale)) return fail(PA_ERR_INVALID_ARGUMENT, "scale must be finite");
   if (num_seqs == 0) return ok();
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
@@ -197,14 +190,11 @@ int pa_decode(void* out, const void* q, int64_t q_seq_stride, const void* k_cach
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || q_seq_stride % 8)
     return fail(PA_ERR_ALIGNMENT, "out, q, caches and q_seq_stride must be 16-byte aligned");
   DecodeGeometry g;
-  decode_geometry(num_seqs, num_q_heads, num_kv_heads, max_context_len, partition_tokens, &g);
-  if (g.num_partitions > 65535) return fail(PA_ERR_UNSUPPORTED, "too many partitions (%d)", g.num_partitions);
-  if (g.ws_bytes > 0) {
-    if (!workspace) return fail(PA_ERR_NULL_POINTER, "workspace of %zu bytes is required", g.ws_bytes);
-    if (workspace_bytes < g.ws_bytes)
-      return fail(PA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < required %zu", workspace_bytes, g.ws_bytes);
-    if (!aligned16(workspace)) return fail(PA_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
-  }
+  decode_geometry(num_seqs, num_q_heads, num_kv_heads, max_context_len, split_waves, &g);
+  if (!workspace) return fail(PA_ERR_NULL_POINTER, "workspace of %zu bytes is required", g.ws_bytes);
+  if (workspace_bytes < g.ws_bytes)
+    return fail(PA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < required %zu", workspace_bytes, g.ws_bytes);
+  if (!aligned16(workspace)) return fail(PA_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
   pa::DecodeArgs a;
   a.out = static_cast<uint16_t*>(out);
   a.q = static_cast<const uint16_t*>(q);
@@ -214,14 +204,13 @@ int pa_decode(void* out, const void* q, int64_t q_seq_stride, const void* k_cach
   a.block_tables = block_tables;
   a.context_lens = context_lens;
   a.ws_o = static_cast<float*>(workspace);
-  a.ws_ml = g.ws_bytes ? reinterpret_cast<float*>(static_cast<char*>(workspace) + g.ws_o_bytes) : nullptr;
+  a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + g.ws_o_bytes);
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.num_seqs = num_seqs;
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = num_kv_heads;
   a.block_size = block_size;
-  a.partition = g.partition;
-  a.num_partitions = g.num_partitions;
+  a.num_waves = g.num_waves;
   a.scale_log2e = scale * kLog2e;
   return hip_status(pa::launch_decode(a, num_q_heads / num_kv_heads, static_cast<hipStream_t>(stream)),
                     "decode launch");

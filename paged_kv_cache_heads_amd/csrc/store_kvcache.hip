@@ -48,14 +48,14 @@ __global__ __launch_bounds__(kStoreThreads) void store_kvcache_kernel(StoreArgs 
   const bool p3 = store_vector(a, base + 3 * kStoreThreads, total, s3, d3);
   // all loads are issued before the first store
   uint4 v0, v1, v2, v3;
-  if (p0) v0 = *s0;
-  if (p1) v1 = *s1;
-  if (p2) v2 = *s2;
-  if (p3) v3 = *s3;
-  if (p0) *d0 = v0;
-  if (p1) *d1 = v1;
-  if (p2) *d2 = v2;
-  if (p3) *d3 = v3;
+  if (p0) v0 = load16_nt(s0);
+  if (p1) v1 = load16_nt(s1);
+  if (p2) v2 = load16_nt(s2);
+  if (p3) v3 = load16_nt(s3);
+  if (p0) store16_nt(d0, v0);
+  if (p1) store16_nt(d1, v1);
+  if (p2) store16_nt(d2, v2);
+  if (p3) store16_nt(d3, v3);
 }
 
 hipError_t launch_store_kvcache(const StoreArgs& a, hipStream_t stream) {

@@ -97,29 +97,30 @@ def test_decode_validation(lib):
     assert decode(lib, W=7) == INVAL             # 7 * 256 < 2048
     assert decode(lib, B=-1) == INVAL
     assert decode(lib, B=70000) == UNSUP
-    assert decode(lib, part=100) == INVAL
+    assert decode(lib, part=-1) == INVAL
     assert decode(lib, scale=float("nan")) == INVAL
     assert decode(lib, q=None) == NULLP
     assert decode(lib, cl=None) == NULLP
     assert decode(lib, qs=1024) == INVAL
     assert decode(lib, out=A + 2) == ALIGN
-    assert decode(lib, ws=None) == NULLP         # partitions > 1 need a workspace
+    assert decode(lib, ws=None) == NULLP         # the workspace is always required
     assert decode(lib, wsb=16) == WS
     assert decode(lib, ws=A + 4) == ALIGN
     assert decode(lib, B=0, out=None, q=None, kc=None, vc=None, bt=None, cl=None) == PA_OK
 
 
 def test_decode_workspace_size(lib):
-    p = lib.pa_decode_partition_tokens(256, 8, 2048, 0)
-    assert p >= 256 and p % 256 == 0
-    nparts = -(-2048 // p)
-    want = 0 if nparts <= 1 else 256 * 16 * nparts * (128 + 2) * 4
-    assert lib.pa_decode_workspace_size(256, 16, 8, 128, 2048, 0) == want
-    assert lib.pa_decode_workspace_size(256, 16, 8, 128, 2048, 256) == 256 * 16 * 8 * 130 * 4
-    assert lib.pa_decode_workspace_size(4, 16, 8, 128, 200, 256) == 0  # one partition: no workspace
+    # G = 2: 32-token chunks; 256 seqs x 8 kv heads x 64 chunks leave the default 2048 waves
+    assert lib.pa_decode_split_waves(256, 16, 8, 2048, 0) == 2048
+    assert lib.pa_decode_workspace_size(256, 16, 8, 128, 2048, 0) == 2048 * 2 * 2 * (128 + 2) * 4
+    # fewer chunks than waves: one wave per chunk at most (4 x 8 x ceil(200/32) = 224)
+    assert lib.pa_decode_split_waves(4, 16, 8, 200, 256) == 224
+    assert lib.pa_decode_workspace_size(4, 16, 8, 128, 200, 256) == 224 * 2 * 2 * 130 * 4
+    # G = 4: 16-token chunks
+    assert lib.pa_decode_split_waves(1, 32, 8, 100, 0) == 8 * 7
     assert lib.pa_decode_workspace_size(4, 16, 8, 64, 2048, 0) == 0    # unsupported head_dim
-    assert lib.pa_decode_workspace_size(4, 16, 8, 128, 2048, 100) == 0  # bad partition
-    assert lib.pa_decode_partition_tokens(4, 8, 2048, 768) == 768
+    assert lib.pa_decode_workspace_size(4, 16, 8, 128, 2048, -1) == 0  # bad split
+    assert lib.pa_decode_split_waves(4, 16, 8, 2048, 100) == 100
 
 
 def prefill(lib, **kw):

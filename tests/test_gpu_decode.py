@@ -15,7 +15,7 @@ from workloads import configs, tensors
 pytestmark = pytest.mark.gpu
 
 
-def _run(wl, dev, seqs=None, partition_tokens=0, extra_check=None):
+def _run(wl, dev, seqs=None, split_waves=0, extra_check=None):
     """store + decode on the GPU; the oracle repeats both on a host copy of the sampled sequences."""
     batch = tensors.materialize(wl, dev)
     seqs = list(range(wl.num_seqs)) if seqs is None else list(seqs)
@@ -26,7 +26,7 @@ def _run(wl, dev, seqs=None, partition_tokens=0, extra_check=None):
     scale = 1.0 / math.sqrt(wl.head_dim)
     pa.pa_store_kvcache(batch.k_new, batch.v_new, batch.k_cache, batch.v_cache, batch.slot_mapping)
     out = pa.pa_decode(batch.q, batch.k_cache, batch.v_cache, batch.block_tables, batch.context_lens, scale,
-                       wl.max_context_len, partition_tokens=partition_tokens)
+                       wl.max_context_len, split_waves=split_waves)
     torch.cuda.synchronize()
     host.store(k_new, v_new, slots, wl.block_size)
     ref = oracle.decode(q[seqs], host.k, host.v, host.tables, wl.context_lens[seqs], scale)
@@ -55,10 +55,11 @@ def test_decode_config2(dev, seed):
     _run(configs.config2(seed), dev)
 
 
-@pytest.mark.parametrize("partition", [0, 256, 2048])
-def test_decode_config2_partitions(dev, partition):
-    announce(f"decode config 2 partition {partition}")
-    _run(configs.config2(), dev, partition_tokens=partition)
+@pytest.mark.parametrize("waves", [0, 1, 7, 300, 5000])
+def test_decode_config2_splits(dev, waves):
+    # 1 wave: every pair whole; 7..5000: pairs cut across 2 to many waves
+    announce(f"decode config 2 split over {waves} waves")
+    _run(configs.config2(), dev, split_waves=waves)
 
 
 def test_decode_config5_sampled(dev):
@@ -75,13 +76,13 @@ def test_decode_config5_sampled(dev):
 @pytest.mark.parametrize("group", [1, 2, 4, 8])
 @pytest.mark.parametrize("block_size", [64, 256])
 def test_decode_edge_lengths(dev, group, block_size):
-    # empty context, one token, chunk and partition boundaries, a ragged tail
+    # empty context, one token, chunk and share boundaries, a ragged tail
     lens = [0, 1, 2, 63, 64, 65, 255, 256, 257, 511, 512, 513, 1000, 1537]
     announce(f"decode edge lengths G={group} bs={block_size}")
     hkv = 2
     wl = configs.decode_workload("edge", lens, hkv * group, hkv, 128, seed=9, block_size=block_size)
-    for partition in (0, 256, 512):
-        _run(wl, dev, partition_tokens=partition)
+    for waves in (0, 3, 64):
+        _run(wl, dev, split_waves=waves)
 
 
 def test_decode_zero_seqs(dev):
