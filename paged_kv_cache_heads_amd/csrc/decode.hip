@@ -164,9 +164,9 @@ __device__ __forceinline__ void compute_chunk(DecodeState<G>& st, const QRegs<G>
     float x = group8_reduce<TPL>(sc, s);  // score of token (s / kDup) * 8 + r
     x = valid ? x * scale_log2e : -INFINITY;
     const float mnew = fmaxf(st.m[j], group8_max(x));
-    const float p = exp2f(x - mnew);
+    const float p = fast_exp2(x - mnew);
     if (__ballot(mnew != st.m[j])) {
-      const float alpha = exp2f(st.m[j] - mnew);
+      const float alpha = fast_exp2(st.m[j] - mnew);
       st.l[j] *= alpha;
 #pragma unroll
       for (int e = 0; e < 16; ++e) st.acc[j][e] *= alpha;
@@ -288,7 +288,7 @@ __device__ __forceinline__ void finish_piece(const DecodeState<G>& st, const Dec
     M = fmaxf(M, dpp<kDppRor8>(M));
     M = fmaxf(M, __shfl_xor(M, 16));
     M = fmaxf(M, __shfl_xor(M, 32));
-    const float f = exp2f(st.m[j] - M);
+    const float f = fast_exp2(st.m[j] - M);
     float Ls = group8_sum(st.l[j]) * f;
     Ls += dpp<kDppRor8>(Ls);
     Ls += __shfl_xor(Ls, 16);
@@ -472,8 +472,8 @@ __global__ __launch_bounds__(64) void decode_finalize_kernel(DecodeArgs a) {
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) mb = fmaxf(mb, __shfl_xor(mb, off));
       const float mnew = fmaxf(M[j], mb);
-      const float alpha = exp2f(M[j] - mnew);
-      const float f = live ? exp2f(ml.x - mnew) : 0.f;
+      const float alpha = fast_exp2(M[j] - mnew);
+      const float f = live ? fast_exp2(ml.x - mnew) : 0.f;
       float lf = f * ml.y;
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) lf += __shfl_xor(lf, off);

@@ -11,22 +11,41 @@
 // page at hotelren.com/news/2273631, section 4.4: a cached prefix's KV is
 // reused and only the remainder is computed).
 //
-// Design for gfx950:
+// Design for gfx950 (the softmax, not the MFMA, is the scarce resource at
+// head_dim 128: per score the MFMAs do 256 MACs while the vector units must
+// scale, mask, exponentiate and convert it, so the kernel keeps that work to
+// an FMA, an exp and half a convert per score):
 // * One workgroup (4 waves) per (tile of 128/G query positions, kv head,
 //   sequence): it covers all G query heads of the kv head, so every K/V tile
-//   staged in LDS serves 128 query rows. Query tiles are issued longest first.
+//   staged in LDS serves 128 query rows. Workgroups are issued heaviest first
+//   across all sequences (last query tiles, which see the most keys, first).
 // * Each wave owns two 16-row subtiles (one head, 16 positions each).
 // * Scores are computed transposed, Sᵀ = K Qᵀ, with v_mfma_f32_16x16x32_bf16:
-//   K (row-major in LDS) is the A operand, Q (registers) the B operand. The
-//   result leaves each lane with 4 keys of one query, so the row max/sum
-//   need only a 2-step exchange across the 4 lanes of a query, and
-//   exp2(s - m) lands in registers already in the layout of the B operand of
-//   Oᵀ = Vᵀ Pᵀ (the key order inside a 32-key step is permuted consistently
-//   on both operands). Vᵀ is written to LDS transposed, two keys per dword.
-// * The next K/V tile is loaded into registers while the current one is
-//   computed. Tiles that straddle the causal diagonal or the sequence end are
-//   masked by selection (never by multiplication), so stale cache bits
-//   cannot leak into the output; fully visible tiles skip the mask.
+//   K (row-major in LDS) is the A operand, Q (registers) the B operand. Each
+//   lane then holds 16 keys of one query, so the row max needs a 2-step
+//   exchange, and exp2(s - m) lands in registers already in the layout of the
+//   B operand of Oᵀ = Vᵀ Pᵀ (the key order inside a 32-key step is permuted
+//   the same way on both operands). V stays row-major in LDS and its Vᵀ
+//   operand is read with ds_read_b64_tr_b16: inside each 16-lane group, lane
+//   i returns element i % 4 of the 4-element segments addressed by lanes
+//   4j + i / 4 (j = 0..3), so lane L pointing at V[4g + L/4][16 dt + 4 (L%4)]
+//   yields V[4g + j][16 dt + L] for j = 0..3 -- four keys of one dim.
+// * Row sums come out of the MFMA: a ninth 16-row output tile with a constant
+//   all-ones A operand accumulates sum_k P[q][k] with the same rescaling as O,
+//   and sums exactly the bf16-rounded P that the numerator uses.
+// * The running maximum is rescaled lazily: O is rescaled only when a row's
+//   maximum grows by more than 2^8, so p = 2^(s - m) stays below 2^8 and the
+//   rescale is almost never taken after the first tiles.
+// * LDS tiles are XOR-swizzled (no padding) so that the MFMA operand reads and
+//   the staging writes are free of bank conflicts.
+// * K and V tiles stream from global memory straight into a double-buffered
+//   LDS (global_load_lds_dwordx4: each lane's 16 bytes land at base + 16 *
+//   lane), so the next tile is in flight during the current one's math with
+//   no staging registers and one barrier per tile. Tile addresses are a
+//   scalar base plus a per-lane offset. Tiles that straddle the causal
+//   diagonal or the sequence end are masked by selection (never by
+//   multiplication), so stale cache bits cannot leak into the output; fully
+//   visible tiles skip the mask.
 #include <math.h>
 
 #include "common.h"
@@ -36,36 +55,42 @@ namespace pa {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
-constexpr int kPD = 128;          // head_dim
-constexpr int kBN = 64;           // keys per tile
+constexpr int kPD = 128;        // head_dim
+constexpr int kBN = 64;         // keys per tile
 constexpr int kPThreads = 256;
-constexpr int kKStride = kPD + 8;  // bf16 elements per K row in LDS (pad: 16 B)
-constexpr int kVStride = kBN + 8;  // bf16 elements per Vᵀ row in LDS (pad: 16 B)
+constexpr int kTileBytes = kBN * kPD * 2;  // one K or V tile: 16 KiB
+constexpr float kRescaleLog2 = 8.f;        // lazy-rescale threshold, log2 units
 
 __device__ __forceinline__ f32x4_t mfma16x16x32(const uint4& a, const uint4& b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
                                                  0, 0, 0);
 }
 
-// Address of key row t (already clamped to [0, nk)) of kv head kvh.
-__device__ __forceinline__ const bf16_t* key_row(const bf16_t* base, int64_t token_stride, const PrefillArgs& a,
-                                                 int seq, int k_beg, int t, int kvh) {
-  if (a.block_table == nullptr) return base + (int64_t)(k_beg + t) * token_stride + kvh * kPD;
-  const int blk = a.block_table[(int64_t)seq * a.max_blocks_per_seq + t / a.block_size];
-  return base + ((int64_t)blk * a.block_size + t % a.block_size) * ((int64_t)a.num_kv_heads * kPD) + kvh * kPD;
-}
+// Byte offset of 16-byte chunk c of row r in a swizzled 64 x 256 B tile.
+// K: chunk c ^ (r % 16) -- conflict-free for 16 rows reading one chunk.
+// V: chunk c ^ 2 (r % 8) -- conflict-free for the transposed 8-byte reads.
+__device__ __forceinline__ uint32_t k_off(int r, int c) { return r * 256 + ((c ^ (r & 15)) << 4); }
+__device__ __forceinline__ uint32_t v_off(int r, int c) { return r * 256 + ((c ^ ((r & 7) << 1)) << 4); }
 
-template <int G>
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// kRawMax: the scale is positive, so the running maximum is taken on raw
+// scores and the scale folds into the exponent's FMA; otherwise scores are
+// scaled first.
+template <int G, bool kRawMax>
 __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16_t sK[kBN * kKStride];
-  __shared__ __attribute__((aligned(16))) bf16_t sVt[kPD * kVStride];
+  // two buffers of [K tile | V tile]
+  __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * kTileBytes];
 
-  constexpr int QP = 128 / G;   // query positions per workgroup
-  constexpr int PB = QP / 16;   // 16-position subtiles per head
-  const int qtile = a.num_q_tiles - 1 - (int)blockIdx.x;
-  const int kvh = blockIdx.y;
-  const int seq = blockIdx.z;
+  constexpr int QP = 128 / G;  // query positions per workgroup
+  constexpr int PB = QP / 16;  // 16-position subtiles per head
+  const int kvh = blockIdx.x;
+  const int seq = blockIdx.y;
+  const int qtile = a.num_q_tiles - 1 - (int)blockIdx.z;
   const int q_beg = a.cu_seqlens_q[seq];
   const int nq = a.cu_seqlens_q[seq + 1] - q_beg;
   const int k_beg = a.cu_seqlens_k[seq];
@@ -92,63 +117,80 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
     for (int ks = 0; ks < 4; ++ks) qop[u][ks] = load16(qr + ks * 32 + 8 * g);
   }
 
-  // keys this workgroup needs, and the first key any of its queries cannot see
+  // keys this workgroup needs, and the first key some row cannot see
   const int q_last = min(q0 + QP, nq) - 1;
   const int k_end = a.causal ? min(nk, shift + q_last + 1) : nk;
   const int full_below = a.causal ? min(nk, shift + q0 + 1) : nk;  // keys < this are visible to every row
-  const int ntiles = (k_end + kBN - 1) / kBN;
+  const int ntiles = k_end > 0 ? (k_end + kBN - 1) / kBN : 0;
 
-  f32x4_t oacc[2][8];
-  float m[2], l[2];
+  // Oᵀ accumulators: 8 tiles of 16 dims + the row-sum tile
+  f32x4_t oacc[2][9];
+  float m[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     m[u] = kNegBig;
-    l[u] = 0.f;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) oacc[u][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int dt = 0; dt < 9; ++dt) oacc[u][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  // staging assignments: K -> 4 x 16 B per thread; V -> key pair x 16 dims
-  const int kv_key = tid >> 4, kv_c = tid & 15;  // K: keys kv_key + 16*u, chunk kv_c
-  const int v_pair = tid & 31, v_dr = tid >> 5;   // V: keys 2*v_pair, 2*v_pair+1; dims 16*v_dr ..
-  uint4 kreg[4], vreg[4];
+  // Tile staging: DMA instruction n = 4 * wave + u (u < 4) fills 1 KiB of the
+  // tile = rows 4n .. 4n + 3; lane i supplies row 4n + i / 16, physical chunk
+  // i % 16, i.e. the logical chunk that the swizzle maps there.
+  const int64_t kstride = a.block_table ? (int64_t)a.num_kv_heads * kPD : a.k_token_stride;
+  const int64_t vstride = a.block_table ? (int64_t)a.num_kv_heads * kPD : a.v_token_stride;
+  int srow[4];
+  uint32_t kofs[4], vofs[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    srow[u] = 16 * wave + 4 * u + (lane >> 4);
+    const int pc = lane & 15;
+    kofs[u] = (uint32_t)(srow[u] * kstride * 2) + ((pc ^ (srow[u] & 15)) << 4);
+    vofs[u] = (uint32_t)(srow[u] * vstride * 2) + ((pc ^ ((srow[u] & 7) << 1)) << 4);
+  }
 
-  auto load_tile = [&](int t0) {
+  auto issue_tile = [&](int t0, int buf) {
+    // first row of the tile (a tile never crosses a block: block_size % 64 == 0)
+    int64_t krow0, vrow0;
+    if (a.block_table == nullptr) {
+      krow0 = (int64_t)(k_beg + t0) * kstride;
+      vrow0 = (int64_t)(k_beg + t0) * vstride;
+    } else {
+      const int blk = a.block_table[(int64_t)seq * a.max_blocks_per_seq + t0 / a.block_size];
+      krow0 = vrow0 = ((int64_t)blk * a.block_size + t0 % a.block_size) * kstride;
+    }
+    const char* kb = reinterpret_cast<const char*>(a.k + krow0 + kvh * kPD);
+    const char* vb = reinterpret_cast<const char*>(a.v + vrow0 + kvh * kPD);
+    char* kdst = smem + buf * 2 * kTileBytes;
+    char* vdst = kdst + kTileBytes;
+    const int last = nk - 1 - t0;  // rows past it are clamped to it
+    const bool full = last >= kBN - 1;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int t = min(t0 + kv_key + 16 * u, nk - 1);
-      kreg[u] = load16(key_row(a.k, a.k_token_stride, a, seq, k_beg, t, kvh) + kv_c * 8);
-    }
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int t = min(t0 + 2 * v_pair + u, nk - 1);
-      const bf16_t* vr = key_row(a.v, a.v_token_stride, a, seq, k_beg, t, kvh) + v_dr * 16;
-      vreg[2 * u] = load16(vr);
-      vreg[2 * u + 1] = load16(vr + 8);
+      uint32_t ko = kofs[u], vo = vofs[u];
+      if (!full && srow[u] > last) {
+        const int pc = lane & 15;
+        ko = (uint32_t)(last * kstride * 2) + ((pc ^ (srow[u] & 15)) << 4);
+        vo = (uint32_t)(last * vstride * 2) + ((pc ^ ((srow[u] & 7) << 1)) << 4);
+      }
+      const int n = 4 * wave + u;
+      __builtin_amdgcn_global_load_lds(kb + ko, (lds_void_t*)(kdst + n * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vb + vo, (lds_void_t*)(vdst + n * 1024), 16, 0, 0);
     }
   };
 
-  const float c = a.scale_log2e;
-  if (ntiles > 0) load_tile(0);
+  // Softmax in log2 units: p = 2^(c*s - c*m).
+  const float c = kRawMax ? a.scale_log2e : 1.f;
+  const float tau = kRescaleLog2 / c;  // threshold in score units
+  const uint4 ones = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);  // bf16 1.0 pairs
+
+  if (ntiles > 0) issue_tile(0, 0);
   for (int tile = 0; tile < ntiles; ++tile) {
     const int t0 = tile * kBN;
-    __syncthreads();  // previous tile fully consumed
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      *reinterpret_cast<uint4*>(&sK[(kv_key + 16 * u) * kKStride + kv_c * 8]) = kreg[u];
-    {
-      const uint32_t* v0 = reinterpret_cast<const uint32_t*>(&vreg[0]);  // key 2p, dims 16*v_dr .. +16
-      const uint32_t* v1 = reinterpret_cast<const uint32_t*>(&vreg[2]);  // key 2p+1
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t lo = __builtin_amdgcn_perm(v1[e], v0[e], 0x05040100u);  // (v0.lo, v1.lo)
-        const uint32_t hi = __builtin_amdgcn_perm(v1[e], v0[e], 0x07060302u);  // (v0.hi, v1.hi)
-        *reinterpret_cast<uint32_t*>(&sVt[(v_dr * 16 + 2 * e) * kVStride + 2 * v_pair]) = lo;
-        *reinterpret_cast<uint32_t*>(&sVt[(v_dr * 16 + 2 * e + 1) * kVStride + 2 * v_pair]) = hi;
-      }
-    }
-    __syncthreads();
-    if (tile + 1 < ntiles) load_tile(t0 + kBN);
+    wait_vmem();      // this wave's part of the tile has landed
+    __syncthreads();  // every wave's part has; the other buffer is free again
+    if (tile + 1 < ntiles) issue_tile(t0 + kBN, (tile + 1) & 1);
+    const char* sK = smem + (tile & 1) * 2 * kTileBytes;
+    const char* sV = sK + kTileBytes;
 
     // ---- Sᵀ = K Qᵀ for both subtiles ----
     f32x4_t sacc[2][4];
@@ -160,48 +202,49 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
     for (int kt = 0; kt < 4; ++kt) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const uint4 kop = *reinterpret_cast<const uint4*>(&sK[(kt * 16 + col) * kKStride + ks * 32 + 8 * g]);
+        const uint4 kop = *reinterpret_cast<const uint4*>(sK + k_off(kt * 16 + col, ks * 4 + g));
         sacc[0][kt] = mfma16x16x32(kop, qop[0][ks], sacc[0][kt]);
         sacc[1][kt] = mfma16x16x32(kop, qop[1][ks], sacc[1][kt]);
       }
     }
 
-    // ---- online softmax (each lane: one query, keys kt*16 + 4g + i) ----
+    // ---- softmax numerators (each lane: one query, keys kt*16 + 4g + i) ----
     const bool need_mask = (t0 + kBN > full_below);
     uint4 pop[2][2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       float x[4][4];
-      float mx = kNegBig;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float v = sacc[u][kt][i] * c;
-          if (need_mask) {
+        for (int i = 0; i < 4; ++i) x[kt][i] = kRawMax ? sacc[u][kt][i] : sacc[u][kt][i] * a.scale_log2e;
+      if (need_mask) {
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
             const int t = t0 + kt * 16 + 4 * g + i;
-            v = (t <= lim[u] && t < nk) ? v : -INFINITY;
+            x[kt][i] = (t <= lim[u] && t < nk) ? x[kt][i] : -INFINITY;
           }
-          x[kt][i] = v;
-          mx = fmaxf(mx, v);
-        }
+      }
+      float mx = fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3]));
+#pragma unroll
+      for (int kt = 1; kt < 4; ++kt) mx = fmaxf(mx, fmaxf(fmaxf(x[kt][0], x[kt][1]), fmaxf(x[kt][2], x[kt][3])));
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(m[u], mx);
-      const float alpha = exp2f(m[u] - mnew);
-      m[u] = mnew;
-      float ps = 0.f;
+      if (__ballot(mx > m[u] + tau)) {
+        const float mnew = fmaxf(m[u], mx);
+        const float alpha = fast_exp2((m[u] - mnew) * c);
+#pragma unroll
+        for (int dt = 0; dt < 9; ++dt) oacc[u][dt] *= alpha;
+        m[u] = mnew;
+      }
+      const float mc = m[u] * c;
       float p[4][4];
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[kt][i] = exp2f(x[kt][i] - mnew);
-          ps += p[kt][i];
-        }
-      l[u] = l[u] * alpha + ps;
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) oacc[u][dt] *= alpha;
+        for (int i = 0; i < 4; ++i) p[kt][i] = fast_exp2(fmaf(x[kt][i], c, -mc));
       // B operand of Oᵀ = Vᵀ Pᵀ for 32-key step kk: slots 0..3 <- tile 2kk, slots 4..7 <- tile 2kk+1
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
@@ -212,29 +255,35 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
       }
     }
 
-    // ---- Oᵀ += Vᵀ Pᵀ ----
+    // ---- Oᵀ += Vᵀ Pᵀ, and the row sums ----
+    const int trow = 4 * g + (col >> 2);  // key row this lane addresses inside a 16-key half
+    const int tq = col & 3;               // which 4-dim segment
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const bf16_t* vrow = &sVt[(dt * 16 + col) * kVStride + kk * 32 + 4 * g];
-        uint4 vop;
-        const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
-        vop.x = lo.x; vop.y = lo.y; vop.z = hi.x; vop.w = hi.y;
+        const int r0 = kk * 32 + trow, r1 = r0 + 16;
+        const int ch = 2 * dt + (tq >> 1), half = (tq & 1) * 8;
+        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(sV + v_off(r0, ch) + half));
+        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(sV + v_off(r1, ch) + half));
+        const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+        const uint4 vop = make_uint4(l2.x, l2.y, h2.x, h2.y);
         oacc[0][dt] = mfma16x16x32(vop, pop[0][kk], oacc[0][dt]);
         oacc[1][dt] = mfma16x16x32(vop, pop[1][kk], oacc[1][dt]);
       }
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      oacc[0][8] = mfma16x16x32(ones, pop[0][kk], oacc[0][8]);
+      oacc[1][8] = mfma16x16x32(ones, pop[1][kk], oacc[1][8]);
     }
   }
 
   // ---- epilogue: normalise and write the rows that exist ----
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    float ls = l[u];
-    ls += __shfl_xor(ls, 16);
-    ls += __shfl_xor(ls, 32);
     if (qpos[u] >= nq) continue;
+    const float ls = oacc[u][8][0];
     const float inv = ls > 0.f ? 1.f / ls : 0.f;
     bf16_t* orow = a.out + ((int64_t)(q_beg + qpos[u]) * a.num_q_heads + head[u]) * kPD;
 #pragma unroll
@@ -249,8 +298,12 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
 
 template <int G>
 static hipError_t launch_prefill_g(const PrefillArgs& a, hipStream_t stream) {
-  dim3 grid(a.num_q_tiles, a.num_kv_heads, a.num_seqs);
-  hipLaunchKernelGGL(prefill_kernel<G>, grid, dim3(kPThreads), 0, stream, a);
+  // x: kv head, y: sequence, z: query tile counted from the last (heaviest) one
+  dim3 grid(a.num_kv_heads, a.num_seqs, a.num_q_tiles);
+  if (a.scale_log2e > 0.f)
+    prefill_kernel<G, true><<<grid, dim3(kPThreads), 0, stream>>>(a);
+  else
+    prefill_kernel<G, false><<<grid, dim3(kPThreads), 0, stream>>>(a);
   return hipGetLastError();
 }
 
