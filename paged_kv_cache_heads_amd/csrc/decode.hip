@@ -378,15 +378,17 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(G >= 8 ? 1 :
   const uint32_t row_bytes = (uint32_t)a.num_kv_heads * kD * 2;
   const uint32_t lane_off = r * row_bytes + 16 * s;
   ChunkRegs<TPL> c0, c1;
-  QRegs<G> q0, q1;
+  QRegs<G> q;
   DecodeState<G> st;
   load_chunk(c0, a, cur, row_bytes, lane_off, r, s);
-  load_q(q0, a, cur.b, cur.g, s);
+  load_q(q, a, cur.b, cur.g, s);
   reset_state(st);
   int k0 = cur.k;  // first chunk of the current piece
   const float sc = a.scale_log2e;
 
-  // Two stages with the register sets swapped (no copies between them).
+  // Two stages with the register sets swapped (no copies between them). The
+  // query of a new pair is loaded when its first chunk is reached (about once
+  // per wave), which keeps the wave within two waves per SIMD of registers.
   for (int64_t c = lo;;) {
     {
       const bool more = c + 1 < hi;
@@ -396,15 +398,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(G >= 8 ? 1 :
         nxt = next_pos(cur, a, CH);
         new_pair = nxt.b != cur.b || nxt.g != cur.g;
         load_chunk(c1, a, nxt, row_bytes, lane_off, r, s);
-        if (new_pair) load_q(q1, a, nxt.b, nxt.g, s);
       }
-      compute_chunk<G, TPL>(st, q0, c0, cur.len - cur.k * CH, sc, lane, r, s);
+      compute_chunk<G, TPL>(st, q, c0, cur.len - cur.k * CH, sc, lane, r, s);
       if (!more || new_pair) {
         finish_piece<G>(st, a, cur, k0, wave, lane, s);
         if (!more) break;
         reset_state(st);
         k0 = 0;
-        q0 = q1;
+        load_q(q, a, nxt.b, nxt.g, s);
       }
       cur = nxt;
       ++c;
@@ -417,15 +418,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(G >= 8 ? 1 :
         nxt = next_pos(cur, a, CH);
         new_pair = nxt.b != cur.b || nxt.g != cur.g;
         load_chunk(c0, a, nxt, row_bytes, lane_off, r, s);
-        if (new_pair) load_q(q1, a, nxt.b, nxt.g, s);
       }
-      compute_chunk<G, TPL>(st, q0, c1, cur.len - cur.k * CH, sc, lane, r, s);
+      compute_chunk<G, TPL>(st, q, c1, cur.len - cur.k * CH, sc, lane, r, s);
       if (!more || new_pair) {
         finish_piece<G>(st, a, cur, k0, wave, lane, s);
         if (!more) break;
         reset_state(st);
         k0 = 0;
-        q0 = q1;
+        load_q(q, a, nxt.b, nxt.g, s);
       }
       cur = nxt;
       ++c;
