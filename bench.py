@@ -94,6 +94,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--split-waves", type=int, default=0, help="decode work split (0 = library choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after timing, run one 256 MiB device copy (reads and writes a known byte count) "
+                         "so that profiler byte counters can be calibrated against it")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this build measures one GPU only; the path is data-parallel and shards by "
@@ -128,10 +131,10 @@ def main():
                                        out=out2, workspace=ws, split_waves=args.split_waves),
         "store_prefill": lambda: pa.pa_store_kvcache(b3.k_new, b3.v_new, b3.k_cache, b3.v_cache, b3.slot_mapping),
         "prefill": lambda: pa.pa_prefill_varlen(b3.q, b3.k_new, b3.v_new, b3.cu_seqlens_q, b3.cu_seqlens_k, mq3,
-                                                scale, out=out3),
+                                                wl3.max_seqlen_k, scale, out=out3),
         "store_prefix": lambda: pa.pa_store_kvcache(b4.k_new, b4.v_new, b4.k_cache, b4.v_cache, b4.slot_mapping),
         "prefill_prefix": lambda: pa.pa_prefill_varlen(b4.q, b4.k_cache, b4.v_cache, b4.cu_seqlens_q,
-                                                       b4.cu_seqlens_k, mq4, scale, block_table=b4.block_tables,
+                                                       b4.cu_seqlens_k, mq4, wl4.max_seqlen_k, scale, block_table=b4.block_tables,
                                                        out=out4),
     }
 
@@ -204,6 +207,11 @@ def main():
         "kernels_us": {k: round(v * 1e3, 2) for k, v in ms.items()},
         "store_GBs": {k: round(sb[k] / (ms[k] * 1e-3) / 1e9, 1) for k in sb},
     }
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(b2, wl2)
     print(json.dumps(result), flush=True)

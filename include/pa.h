@@ -171,12 +171,15 @@ int pa_decode(void* out, const void* q, int64_t q_seq_stride, const void* k_cach
  *               block_table[i, t / block_size].
  * cu_seqlens_q, cu_seqlens_k  [num_seqs + 1] int32, non-decreasing from 0.
  * max_seqlen_q  upper bound of every nq (sizes the launch grid).
+ * max_seqlen_k  upper bound of every nk; selects the key tile (32 keys up to
+ *               1024, else 64). It only affects speed: results are correct
+ *               for any value.
  * block_table   optional [num_seqs, max_blocks_per_seq] int32.
  */
 int pa_prefill_varlen(void* out, const void* q, int64_t q_token_stride, const void* k, const void* v,
                       int64_t k_token_stride, int64_t v_token_stride, const int32_t* cu_seqlens_q,
-                      const int32_t* cu_seqlens_k, int32_t num_seqs, int32_t max_seqlen_q, int32_t num_q_heads,
-                      int32_t num_kv_heads, int32_t head_dim, float scale, int32_t causal,
+                      const int32_t* cu_seqlens_k, int32_t num_seqs, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, float scale, int32_t causal,
                       const int32_t* block_table, int32_t max_blocks_per_seq, int32_t block_size, void* stream);
 
 #ifdef __cplusplus

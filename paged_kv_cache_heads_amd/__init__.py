@@ -112,8 +112,8 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, max
     return out
 
 
-def pa_prefill_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, scale: float, causal: bool = True,
-                      block_table=None, out=None, stream=None):
+def pa_prefill_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int, scale: float,
+                      causal: bool = True, block_table=None, out=None, stream=None):
     """Varlen prefill: q [Tq, Hq, D] bf16 -> out [Tq, Hq, D] bf16.
 
     Without block_table, k / v are packed [Tk, Hkv, D] (row strides may exceed
@@ -131,6 +131,7 @@ def pa_prefill_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, sc
         ks, vs, width = hkv * d, hkv * d, int(block_table.shape[1])
     _check("pa_prefill_varlen", lib.pa_prefill_varlen(
         _ptr(out), _ptr(q), _rows(q, "q"), _ptr(k), _ptr(v), ks, vs, _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
-        int(cu_seqlens_q.shape[0]) - 1, int(max_seqlen_q), hq, hkv, d, float(scale), 1 if causal else 0,
+        int(cu_seqlens_q.shape[0]) - 1, int(max_seqlen_q), int(max_seqlen_k), hq, hkv, d, float(scale),
+        1 if causal else 0,
         _ptr(block_table), width, bs, _stream(stream, q.device)))
     return out

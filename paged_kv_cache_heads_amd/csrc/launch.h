@@ -53,6 +53,7 @@ struct PrefillArgs {
   int32_t block_size;
   int32_t num_seqs;
   int32_t num_q_tiles;
+  int32_t max_seqlen_k;
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t causal;
@@ -68,5 +69,8 @@ hipError_t launch_prefill(const PrefillArgs& a, int group, hipStream_t stream);
 
 // Query positions covered by one prefill workgroup for a GQA group size.
 inline int prefill_tile_positions(int group) { return 128 / group; }
+// Keys per prefill tile: 32 while sequences are short (at most 1024 keys),
+// else 64.
+inline int prefill_key_tile(int max_seqlen_k) { return max_seqlen_k <= 1024 ? 32 : 64; }
 
 }  // namespace pa

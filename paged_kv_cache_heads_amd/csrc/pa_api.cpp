@@ -218,11 +218,12 @@ int pa_decode(void* out, const void* q, int64_t q_seq_stride, const void* k_cach
 
 int pa_prefill_varlen(void* out, const void* q, int64_t q_token_stride, const void* k, const void* v,
                       int64_t k_token_stride, int64_t v_token_stride, const int32_t* cu_seqlens_q,
-                      const int32_t* cu_seqlens_k, int32_t num_seqs, int32_t max_seqlen_q, int32_t num_q_heads,
-                      int32_t num_kv_heads, int32_t head_dim, float scale, int32_t causal,
+                      const int32_t* cu_seqlens_k, int32_t num_seqs, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, float scale, int32_t causal,
                       const int32_t* block_table, int32_t max_blocks_per_seq, int32_t block_size, void* stream) {
-  if (num_seqs < 0 || max_seqlen_q < 0)
-    return fail(PA_ERR_INVALID_ARGUMENT, "num_seqs (%d) and max_seqlen_q (%d) must be >= 0", num_seqs, max_seqlen_q);
+  if (num_seqs < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "num_seqs (%d), max_seqlen_q (%d) and max_seqlen_k (%d) must be >= 0",
+                num_seqs, max_seqlen_q, max_seqlen_k);
   if (num_seqs > 65535) return fail(PA_ERR_UNSUPPORTED, "num_seqs %d exceeds 65535", num_seqs);
   int st = check_heads(num_q_heads, num_kv_heads, head_dim);
   if (st) return st;
@@ -266,6 +267,7 @@ int pa_prefill_varlen(void* out, const void* q, int64_t q_token_stride, const vo
   a.block_size = block_table ? block_size : 0;
   a.num_seqs = num_seqs;
   a.num_q_tiles = (max_seqlen_q + qp - 1) / qp;
+  a.max_seqlen_k = max_seqlen_k;
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = num_kv_heads;
   a.causal = causal ? 1 : 0;

@@ -60,10 +60,8 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
 constexpr int kPD = 128;        // head_dim
-constexpr int kBN = 64;         // keys per tile
 constexpr int kPThreads = 256;
-constexpr int kTileBytes = kBN * kPD * 2;  // one K or V tile: 16 KiB
-constexpr float kRescaleLog2 = 8.f;        // lazy-rescale threshold, log2 units
+constexpr float kRescaleLog2 = 8.f;  // lazy-rescale threshold, log2 units
 
 __device__ __forceinline__ f32x4_t mfma16x16x32(const uint4& a, const uint4& b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
@@ -80,9 +78,17 @@ __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" 
 
 // kRawMax: the scale is positive, so the running maximum is taken on raw
 // scores and the scale folds into the exponent's FMA; otherwise scores are
-// scaled first.
-template <int G, bool kRawMax>
-__global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
+// scaled first. BN: keys per tile, 64 (2 waves per SIMD) or 32 (half the
+// score registers and LDS, 3 waves per SIMD: finer causal steps and more
+// latency hiding for short sequences).
+template <int G, bool kRawMax, int BN>
+__global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(BN == 32 ? 3 : 2, 8)))
+void prefill_kernel(PrefillArgs a) {
+  constexpr int kBN = BN;
+  constexpr int KT = BN / 16;                // 16-key score tiles per tile
+  constexpr int KK = BN / 32;                // 32-key steps of the PV product
+  constexpr int DU = BN / 16;                // 1 KiB DMA instructions per wave per K (or V) tile
+  constexpr int kTileBytes = BN * kPD * 2;   // one K or V tile
   // two buffers of [K tile | V tile]
   __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * kTileBytes];
 
@@ -133,16 +139,16 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
     for (int dt = 0; dt < 9; ++dt) oacc[u][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  // Tile staging: DMA instruction n = 4 * wave + u (u < 4) fills 1 KiB of the
-  // tile = rows 4n .. 4n + 3; lane i supplies row 4n + i / 16, physical chunk
-  // i % 16, i.e. the logical chunk that the swizzle maps there.
+  // Tile staging: DMA instruction n = DU * wave + u (u < DU) fills 1 KiB of
+  // the tile = rows 4n .. 4n + 3; lane i supplies row 4n + i / 16, physical
+  // chunk i % 16, i.e. the logical chunk that the swizzle maps there.
   const int64_t kstride = a.block_table ? (int64_t)a.num_kv_heads * kPD : a.k_token_stride;
   const int64_t vstride = a.block_table ? (int64_t)a.num_kv_heads * kPD : a.v_token_stride;
-  int srow[4];
-  uint32_t kofs[4], vofs[4];
+  int srow[DU];
+  uint32_t kofs[DU], vofs[DU];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    srow[u] = 16 * wave + 4 * u + (lane >> 4);
+  for (int u = 0; u < DU; ++u) {
+    srow[u] = 4 * (DU * wave + u) + (lane >> 4);
     const int pc = lane & 15;
     kofs[u] = (uint32_t)(srow[u] * kstride * 2) + ((pc ^ (srow[u] & 15)) << 4);
     vofs[u] = (uint32_t)(srow[u] * vstride * 2) + ((pc ^ ((srow[u] & 7) << 1)) << 4);
@@ -165,14 +171,14 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
     const int last = nk - 1 - t0;  // rows past it are clamped to it
     const bool full = last >= kBN - 1;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < DU; ++u) {
       uint32_t ko = kofs[u], vo = vofs[u];
       if (!full && srow[u] > last) {
         const int pc = lane & 15;
         ko = (uint32_t)(last * kstride * 2) + ((pc ^ (srow[u] & 15)) << 4);
         vo = (uint32_t)(last * vstride * 2) + ((pc ^ ((srow[u] & 7) << 1)) << 4);
       }
-      const int n = 4 * wave + u;
+      const int n = DU * wave + u;
       __builtin_amdgcn_global_load_lds(kb + ko, (lds_void_t*)(kdst + n * 1024), 16, 0, 0);
       __builtin_amdgcn_global_load_lds(vb + vo, (lds_void_t*)(vdst + n * 1024), 16, 0, 0);
     }
@@ -192,44 +198,45 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
     const char* sK = smem + (tile & 1) * 2 * kTileBytes;
     const char* sV = sK + kTileBytes;
 
-    // ---- Sᵀ = K Qᵀ for both subtiles ----
-    f32x4_t sacc[2][4];
+    // ---- Sᵀ = K Qᵀ for both subtiles (8 independent accumulators per k-step) ----
+    f32x4_t sacc[2][KT];
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) sacc[u][kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int kt = 0; kt < KT; ++kt) sacc[u][kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
+    for (int ks = 0; ks < 4; ++ks) {
+      uint4 kop[KT];
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const uint4 kop = *reinterpret_cast<const uint4*>(sK + k_off(kt * 16 + col, ks * 4 + g));
-        sacc[0][kt] = mfma16x16x32(kop, qop[0][ks], sacc[0][kt]);
-        sacc[1][kt] = mfma16x16x32(kop, qop[1][ks], sacc[1][kt]);
+      for (int kt = 0; kt < KT; ++kt) kop[kt] = *reinterpret_cast<const uint4*>(sK + k_off(kt * 16 + col, ks * 4 + g));
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+        sacc[0][kt] = mfma16x16x32(kop[kt], qop[0][ks], sacc[0][kt]);
+        sacc[1][kt] = mfma16x16x32(kop[kt], qop[1][ks], sacc[1][kt]);
       }
     }
 
     // ---- softmax numerators (each lane: one query, keys kt*16 + 4g + i) ----
     const bool need_mask = (t0 + kBN > full_below);
-    uint4 pop[2][2];
+    uint4 pop[2][KK];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      float x[4][4];
+      float x[KT][4];
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
+      for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) x[kt][i] = kRawMax ? sacc[u][kt][i] : sacc[u][kt][i] * a.scale_log2e;
       if (need_mask) {
+        // key t0 + kt*16 + 4g + i is visible iff kt*16 + i <= rel
+        const int rel = min(lim[u], nk - 1) - t0 - 4 * g;
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
+        for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int t = t0 + kt * 16 + 4 * g + i;
-            x[kt][i] = (t <= lim[u] && t < nk) ? x[kt][i] : -INFINITY;
-          }
+          for (int i = 0; i < 4; ++i) x[kt][i] = (kt * 16 + i <= rel) ? x[kt][i] : -INFINITY;
       }
       float mx = fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3]));
 #pragma unroll
-      for (int kt = 1; kt < 4; ++kt) mx = fmaxf(mx, fmaxf(fmaxf(x[kt][0], x[kt][1]), fmaxf(x[kt][2], x[kt][3])));
+      for (int kt = 1; kt < KT; ++kt) mx = fmaxf(mx, fmaxf(fmaxf(x[kt][0], x[kt][1]), fmaxf(x[kt][2], x[kt][3])));
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       if (__ballot(mx > m[u] + tau)) {
@@ -240,14 +247,14 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
         m[u] = mnew;
       }
       const float mc = m[u] * c;
-      float p[4][4];
+      float p[KT][4];
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
+      for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) p[kt][i] = fast_exp2(fmaf(x[kt][i], c, -mc));
       // B operand of Oᵀ = Vᵀ Pᵀ for 32-key step kk: slots 0..3 <- tile 2kk, slots 4..7 <- tile 2kk+1
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
+      for (int kk = 0; kk < KK; ++kk) {
         pop[u][kk].x = pack_bf16x2(p[2 * kk][0], p[2 * kk][1]);
         pop[u][kk].y = pack_bf16x2(p[2 * kk][2], p[2 * kk][3]);
         pop[u][kk].z = pack_bf16x2(p[2 * kk + 1][0], p[2 * kk + 1][1]);
@@ -255,14 +262,14 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
       }
     }
 
-    // ---- Oᵀ += Vᵀ Pᵀ, and the row sums ----
+    // ---- Oᵀ += Vᵀ Pᵀ, and the row sums (16 independent accumulators per k-step) ----
     const int trow = 4 * g + (col >> 2);  // key row this lane addresses inside a 16-key half
     const int tq = col & 3;               // which 4-dim segment
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
+    for (int kk = 0; kk < KK; ++kk) {
+      const int r0 = kk * 32 + trow, r1 = r0 + 16;
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const int r0 = kk * 32 + trow, r1 = r0 + 16;
+      for (int dt = 0; dt < 8; ++dt) {
         const int ch = 2 * dt + (tq >> 1), half = (tq & 1) * 8;
         const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(sV + v_off(r0, ch) + half));
         const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(sV + v_off(r1, ch) + half));
@@ -271,9 +278,6 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
         oacc[0][dt] = mfma16x16x32(vop, pop[0][kk], oacc[0][dt]);
         oacc[1][dt] = mfma16x16x32(vop, pop[1][kk], oacc[1][dt]);
       }
-    }
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
       oacc[0][8] = mfma16x16x32(ones, pop[0][kk], oacc[0][8]);
       oacc[1][8] = mfma16x16x32(ones, pop[1][kk], oacc[1][8]);
     }
@@ -296,14 +300,22 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
   }
 }
 
-template <int G>
-static hipError_t launch_prefill_g(const PrefillArgs& a, hipStream_t stream) {
+template <int G, int BN>
+static void launch_prefill_gb(const PrefillArgs& a, hipStream_t stream) {
   // x: kv head, y: sequence, z: query tile counted from the last (heaviest) one
   dim3 grid(a.num_kv_heads, a.num_seqs, a.num_q_tiles);
   if (a.scale_log2e > 0.f)
-    prefill_kernel<G, true><<<grid, dim3(kPThreads), 0, stream>>>(a);
+    prefill_kernel<G, true, BN><<<grid, dim3(kPThreads), 0, stream>>>(a);
   else
-    prefill_kernel<G, false><<<grid, dim3(kPThreads), 0, stream>>>(a);
+    prefill_kernel<G, false, BN><<<grid, dim3(kPThreads), 0, stream>>>(a);
+}
+
+template <int G>
+static hipError_t launch_prefill_g(const PrefillArgs& a, hipStream_t stream) {
+  if (prefill_key_tile(a.max_seqlen_k) == 32)
+    launch_prefill_gb<G, 32>(a, stream);
+  else
+    launch_prefill_gb<G, 64>(a, stream);
   return hipGetLastError();
 }
 

@@ -124,12 +124,12 @@ def test_decode_workspace_size(lib):
 
 
 def prefill(lib, **kw):
-    a = dict(out=A, q=A, qs=2048, k=A, v=A, ks=3072, vs=3072, cq=A, ck=A, S=4, maxq=1024, hq=16, hkv=8, d=128,
-             scale=0.088, causal=1, bt=None, W=0, bs=0, stream=None)
+    a = dict(out=A, q=A, qs=2048, k=A, v=A, ks=3072, vs=3072, cq=A, ck=A, S=4, maxq=1024, maxk=1024, hq=16, hkv=8,
+             d=128, scale=0.088, causal=1, bt=None, W=0, bs=0, stream=None)
     a.update(kw)
     return lib.pa_prefill_varlen(a["out"], a["q"], a["qs"], a["k"], a["v"], a["ks"], a["vs"], a["cq"], a["ck"],
-                                 a["S"], a["maxq"], a["hq"], a["hkv"], a["d"], a["scale"], a["causal"], a["bt"],
-                                 a["W"], a["bs"], a["stream"])
+                                 a["S"], a["maxq"], a["maxk"], a["hq"], a["hkv"], a["d"], a["scale"], a["causal"],
+                                 a["bt"], a["W"], a["bs"], a["stream"])
 
 
 def test_prefill_validation(lib):
@@ -137,6 +137,7 @@ def test_prefill_validation(lib):
     assert prefill(lib, d=256) == UNSUP
     assert prefill(lib, S=-2) == INVAL
     assert prefill(lib, maxq=-1) == INVAL
+    assert prefill(lib, maxk=-1) == INVAL
     assert prefill(lib, ks=512) == INVAL
     assert prefill(lib, vs=1028) == ALIGN
     assert prefill(lib, cq=None) == NULLP

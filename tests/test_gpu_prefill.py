@@ -15,17 +15,21 @@ from workloads import configs, tensors
 pytestmark = pytest.mark.gpu
 
 
-def _packed(wl, dev, causal=True, check_table_path=True):
-    """Prefill over packed q/k/v; the same keys read back through the cache must give identical bits."""
+def _packed(wl, dev, causal=True, check_table_path=True, max_k=None):
+    """Prefill over packed q/k/v; the same keys read back through the cache must give identical bits.
+
+    max_k overrides the max_seqlen_k hint, which only picks the key tile (1 -> 32 keys, 4096 -> 64 keys).
+    """
+    mk = wl.max_seqlen_k if max_k is None else max_k
     batch = tensors.materialize(wl, dev)
     scale = 1.0 / math.sqrt(wl.head_dim)
     pa.pa_store_kvcache(batch.k_new, batch.v_new, batch.k_cache, batch.v_cache, batch.slot_mapping)
     out = pa.pa_prefill_varlen(batch.q, batch.k_new, batch.v_new, batch.cu_seqlens_q, batch.cu_seqlens_k,
-                               wl.max_seqlen_q, scale, causal=causal)
+                               wl.max_seqlen_q, mk, scale, causal=causal)
     out_t = None
     if check_table_path:
         out_t = pa.pa_prefill_varlen(batch.q, batch.k_cache, batch.v_cache, batch.cu_seqlens_q, batch.cu_seqlens_k,
-                                     wl.max_seqlen_q, scale, causal=causal, block_table=batch.block_tables)
+                                     wl.max_seqlen_q, mk, scale, causal=causal, block_table=batch.block_tables)
     torch.cuda.synchronize()
     ref = oracle.prefill_varlen(tensors.to_u16(batch.q), tensors.to_u16(batch.k_new), tensors.to_u16(batch.v_new),
                                 wl.cu_seqlens_q, wl.cu_seqlens_k, scale, causal=causal)
@@ -35,8 +39,9 @@ def _packed(wl, dev, causal=True, check_table_path=True):
     return stats
 
 
-def _table(wl, dev, causal=True):
+def _table(wl, dev, causal=True, max_k=None):
     """store the new tokens, then prefill through the block table (prefix blocks shared)."""
+    mk = wl.max_seqlen_k if max_k is None else max_k
     batch = tensors.materialize(wl, dev)
     scale = 1.0 / math.sqrt(wl.head_dim)
     host = Compact(batch, range(wl.num_seqs))  # pre-store contents
@@ -44,7 +49,7 @@ def _table(wl, dev, causal=True):
     slots = batch.slot_mapping.cpu().numpy()
     pa.pa_store_kvcache(batch.k_new, batch.v_new, batch.k_cache, batch.v_cache, batch.slot_mapping)
     out = pa.pa_prefill_varlen(batch.q, batch.k_cache, batch.v_cache, batch.cu_seqlens_q, batch.cu_seqlens_k,
-                               wl.max_seqlen_q, scale, causal=causal, block_table=batch.block_tables)
+                               wl.max_seqlen_q, mk, scale, causal=causal, block_table=batch.block_tables)
     torch.cuda.synchronize()
     host.store(k_new, v_new, slots, wl.block_size)
     ref = oracle.prefill_varlen(tensors.to_u16(batch.q), host.k, host.v, wl.cu_seqlens_q, wl.cu_seqlens_k, scale,
@@ -52,37 +57,39 @@ def _table(wl, dev, causal=True):
     return assert_attention_close(out, ref, wl.name)
 
 
-@pytest.mark.parametrize("seed", [3, 101])
-def test_prefill_config3(dev, seed):
-    announce(f"prefill config 3 seed {seed}")
-    _packed(configs.config3(seed), dev)
+@pytest.mark.parametrize("seed,max_k", [(3, None), (101, None), (3, 4096)])
+def test_prefill_config3(dev, seed, max_k):
+    announce(f"prefill config 3 seed {seed} max_k {max_k}")
+    _packed(configs.config3(seed), dev, max_k=max_k)
 
 
-@pytest.mark.parametrize("seed", [4, 102])
-def test_prefill_config4(dev, seed):
-    announce(f"prefill config 4 seed {seed}")
-    _table(configs.config4(seed), dev)
+@pytest.mark.parametrize("seed,max_k", [(4, None), (102, None), (4, 1)])
+def test_prefill_config4(dev, seed, max_k):
+    announce(f"prefill config 4 seed {seed} max_k {max_k}")
+    _table(configs.config4(seed), dev, max_k=max_k)
 
 
+@pytest.mark.parametrize("max_k", [1, 4096])
 @pytest.mark.parametrize("group", [1, 2, 4, 8])
 @pytest.mark.parametrize("causal", [True, False])
-def test_prefill_ragged_small(dev, group, causal):
-    # lengths around tile edges (16, 64, 128/G positions) and single-token sequences
-    lens = [1, 2, 15, 16, 17, 63, 64, 65, 127, 129, 300]
-    announce(f"prefill ragged G={group} causal={causal}")
+def test_prefill_ragged_small(dev, group, causal, max_k):
+    # lengths around tile edges (16, 32, 64, 128/G positions) and single-token sequences
+    lens = [1, 2, 15, 16, 17, 31, 33, 63, 64, 65, 127, 129, 300]
+    announce(f"prefill ragged G={group} causal={causal} max_k={max_k}")
     wl = configs.prefill_workload("ragged", lens, 0, 2 * group, 2, 64, seed=21)
-    _packed(wl, dev, causal=causal)
+    _packed(wl, dev, causal=causal, max_k=max_k)
 
 
+@pytest.mark.parametrize("max_k", [1, 4096])
 @pytest.mark.parametrize("block_size", [64, 256])
 @pytest.mark.parametrize("group", [2, 4])
-def test_prefill_prefix_small(dev, block_size, group):
+def test_prefill_prefix_small(dev, block_size, group, max_k):
     # fewer queries than keys: queries are the last positions; prefix blocks shared
-    announce(f"prefill prefix bs={block_size} G={group}")
+    announce(f"prefill prefix bs={block_size} G={group} max_k={max_k}")
     wl = configs.prefill_workload("prefix", [1, 5, 64, 100, 200], 256, 2 * group, 2, 64, seed=22,
                                   block_size=block_size)
-    _table(wl, dev, causal=True)
-    _table(wl, dev, causal=False)
+    _table(wl, dev, causal=True, max_k=max_k)
+    _table(wl, dev, causal=False, max_k=max_k)
 
 
 def test_prefill_empty_sequence_in_batch(dev):
@@ -100,7 +107,7 @@ def test_prefill_last_row_equals_decode(dev):
     scale = 1.0 / math.sqrt(128)
     pa.pa_store_kvcache(batch.k_new, batch.v_new, batch.k_cache, batch.v_cache, batch.slot_mapping)
     out = pa.pa_prefill_varlen(batch.q, batch.k_cache, batch.v_cache, batch.cu_seqlens_q, batch.cu_seqlens_k,
-                               wl.max_seqlen_q, scale, block_table=batch.block_tables)
+                               wl.max_seqlen_q, wl.max_seqlen_k, scale, block_table=batch.block_tables)
     last = torch.tensor(wl.cu_seqlens_q[1:] - 1, dtype=torch.int64, device=dev)
     q_last = batch.q[last].contiguous()
     lens_t = torch.tensor(lens, dtype=torch.int32, device=dev)
