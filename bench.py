@@ -59,6 +59,26 @@ def prefill_flops(wl, causal=True) -> int:
     return pairs * 4 * wl.head_dim * wl.num_q_heads
 
 
+def measured_traffic():
+    """HBM bytes per pa_decode launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    summary, or None if the decode kernel source changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "bench_default_hbm_traffic.md")
+    srcs = [os.path.join(ROOT, "paged_kv_cache_heads_amd", "csrc", n) for n in ("decode.hip", "common.h")]
+    try:
+        rec = None
+        with open(path, encoding="utf-8") as f:
+            for line in f:
+                if line.startswith("traffic_json:"):
+                    rec = json.loads(line.split(":", 1)[1])
+        sha = hashlib.sha256(b"".join(open(p, "rb").read() for p in srcs)).hexdigest()[:16]
+    except OSError:
+        return None
+    if not rec or rec.get("source_sha256_16") != sha:
+        return None
+    return rec["bytes_per_launch"]
+
+
 def cpu_baseline(batch, wl, budget_s=15.0):
     """The fp64 oracle on a bounded prefix of the decode batch, on the host."""
     import threadpoolctl
@@ -194,7 +214,7 @@ def main():
         },
         "roofline": {"bound": "hbm", "kernel": "pa_decode (split + finalize kernels)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "bytes_per_launch": dbytes["total"], "avg_launch_us": round(ms["decode"] * 1e3, 2)},
         "roofline_prefill": {"bound": "mfma", "kernel": "prefill_kernel (varlen, packed)", "achieved": round(t3, 1),
                              "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",

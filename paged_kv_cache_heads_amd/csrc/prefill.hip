@@ -38,15 +38,18 @@
 //   rescale is almost never taken after the first tiles.
 // * LDS tiles are XOR-swizzled (no padding) so that the MFMA operand reads and
 //   the staging writes are free of bank conflicts.
-// * K and V tiles stream from global memory straight into a double-buffered
-//   LDS (global_load_lds_dwordx4: each lane's 16 bytes land at base + 16 *
-//   lane), so the next tile is in flight during the current one's math with
-//   no staging registers and one barrier per tile. Tile addresses are a
+// * K and V tiles stream from global memory straight into LDS ring buffers
+//   (global_load_lds_dwordx4: each lane's 16 bytes land at base + 16 *
+//   lane), so later tiles are in flight during the current one's math with no
+//   staging registers and one barrier per tile (a barrier that does not wait
+//   for the loads still in flight). Tile addresses are a
 //   scalar base plus a per-lane offset. Tiles that straddle the causal
 //   diagonal or the sequence end are masked by selection (never by
 //   multiplication), so stale cache bits cannot leak into the output; fully
 //   visible tiles skip the mask.
 #include <math.h>
+
+#include <type_traits>
 
 #include "common.h"
 #include "launch.h"
@@ -74,7 +77,84 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(const uint4& a, const uint4& b, 
 __device__ __forceinline__ uint32_t k_off(int r, int c) { return r * 256 + ((c ^ (r & 15)) << 4); }
 __device__ __forceinline__ uint32_t v_off(int r, int c) { return r * 256 + ((c ^ ((r & 7) << 1)) << 4); }
 
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Workgroup barrier that does not drain outstanding loads (the tile DMA must
+// stay in flight across it): this wave's LDS reads are complete, then
+// s_barrier. The memory clobber keeps the compiler from moving LDS accesses
+// across it.
+__device__ __forceinline__ void barrier_keep_loads() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Wait until at most N vector-memory instructions of this wave are
+// outstanding (s_waitcnt vmcnt(N); expcnt and lgkmcnt left alone). Issued
+// through the builtin so that the compiler's own wait bookkeeping sees it.
+template <int N>
+__device__ __forceinline__ void wait_vmem_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+template <int B>
+using Buf = std::integral_constant<int, B>;
+
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for_from(F&& f) {
+  if constexpr (I < N) {
+    f(Buf<I>());
+    static_for_from<I + 1, N>(f);
+  }
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) { static_for_from<0, N>(f); }
+
+typedef int v2i_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// ds_read_b64_tr_b16 at addr + OFF. Issued as inline assembly: the compiler's
+// own form of this read carries no aliasing information, so the compiler
+// would make it wait for every tile DMA in flight. Being opaque, it is not
+// counted by the compiler's waits either: results are only used after
+// wait_lds_le has covered them.
+template <int OFF>
+__device__ __forceinline__ v2i_t ds_read_tr_b64(uint32_t addr) {
+  v2i_t r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+
+// s_waitcnt lgkmcnt(N), tied to the registers it makes valid so that no use of
+// them is scheduled above it. Every LDS access issued after the reads being
+// waited for completes after them (LDS returns in order), so extra younger
+// accesses only make the wait stricter; no scalar memory load is issued
+// between these reads and their wait.
+template <int N>
+__device__ __forceinline__ void wait_lds_le(v2i_t& x, v2i_t& y) {
+  static_assert(N >= 0 && N < 16, "lgkmcnt range");
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(x), "+v"(y) : "i"(N));
+}
+
+// Opaque re-definition of register values (no instruction is emitted).
+template <int N>
+__device__ __forceinline__ void launder(uint32_t (&x)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" : "+v"(x[i]));
+}
+
+// Maximum of x over lanes l and l ^ 16 (l ^ 32): the row-swap permutes put
+// each lane's partner value in one of the two results.
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+constexpr int kVWin = 4;  // transposed V read pairs in flight
 
 // kRawMax: the scale is positive, so the running maximum is taken on raw
 // scores and the scale folds into the exponent's FMA; otherwise scores are
@@ -89,8 +169,21 @@ void prefill_kernel(PrefillArgs a) {
   constexpr int KK = BN / 32;                // 32-key steps of the PV product
   constexpr int DU = BN / 16;                // 1 KiB DMA instructions per wave per K (or V) tile
   constexpr int kTileBytes = BN * kPD * 2;   // one K or V tile
-  // two buffers of [K tile | V tile]
-  __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * kTileBytes];
+  // Buffers of [K tile | V tile]: 3 for 32-key tiles (48 KiB, three
+  // workgroups per CU, tiles fetched two ahead), 2 for 64-key tiles (64 KiB,
+  // two workgroups per CU, one ahead).
+  // Each buffer is its own array and every access names it statically, so
+  // the compiler can tell that reads of one buffer do not alias the DMA still
+  // in flight into another and does not wait for that DMA before them.
+  constexpr int STAGES = BN == 32 ? 3 : 2;
+  __shared__ __attribute__((aligned(1024))) char sbuf0[2 * kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char sbuf1[2 * kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char sbuf2[2 * kTileBytes];
+  auto buffer = [&](auto b) -> char* {
+    if constexpr (decltype(b)::value == 0) return sbuf0;
+    else if constexpr (decltype(b)::value == 1) return sbuf1;
+    else return sbuf2;
+  };
 
   constexpr int QP = 128 / G;  // query positions per workgroup
   constexpr int PB = QP / 16;  // 16-position subtiles per head
@@ -154,19 +247,45 @@ void prefill_kernel(PrefillArgs a) {
     vofs[u] = (uint32_t)(srow[u] * vstride * 2) + ((pc ^ ((srow[u] & 7) << 1)) << 4);
   }
 
-  auto issue_tile = [&](int t0, int buf) {
-    // first row of the tile (a tile never crosses a block: block_size % 64 == 0)
+  // Transposed V reads: lane L points at key row 4 g + L / 4 (of a 16-key
+  // half), 4-dim segment L % 4 of dims 16 dt ..; the swizzle only depends on
+  // the row mod 8, so the key offset of a read is an additive constant.
+  // K operand reads: row kt * 16 + col, logical chunk 4 ks + g (swizzled by col).
+  uint32_t koff[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) koff[ks] = k_off(col, ks * 4 + g);
+  uint32_t voff[8];
+  {
+    const int trow = 4 * g + (col >> 2), tq = col & 3;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) voff[dt] = v_off(trow, 2 * dt + (tq >> 1)) + (tq & 1) * 8;
+  }
+
+  // Block-table entries of this sequence, 64 at a time: lane i holds entry
+  // tbase + i (entries past the ones the sequence uses read as 0).
+  const int nblk = a.block_table ? min(a.max_blocks_per_seq, (nk + a.block_size - 1) / max(a.block_size, 1)) : 0;
+  int tbase = 0, tentry = 0;
+  auto load_table = [&](int base) {
+    tbase = base;
+    tentry = base + lane < nblk ? a.block_table[(int64_t)seq * a.max_blocks_per_seq + base + lane] : 0;
+  };
+  if (a.block_table) load_table(0);
+  int iblk = 0, ioff = 0;  // block and offset of the next tile to issue (tiles never straddle a block)
+
+  auto issue_tile = [&](int t0, char* kdst) {
     int64_t krow0, vrow0;
     if (a.block_table == nullptr) {
       krow0 = (int64_t)(k_beg + t0) * kstride;
       vrow0 = (int64_t)(k_beg + t0) * vstride;
     } else {
-      const int blk = a.block_table[(int64_t)seq * a.max_blocks_per_seq + t0 / a.block_size];
-      krow0 = vrow0 = ((int64_t)blk * a.block_size + t0 % a.block_size) * kstride;
+      if (iblk - tbase >= 64) load_table(iblk);
+      const int blk = __builtin_amdgcn_readlane(tentry, iblk - tbase);
+      krow0 = vrow0 = ((int64_t)blk * a.block_size + ioff) * kstride;
+      ioff += kBN;
+      if (ioff == a.block_size) ioff = 0, ++iblk;
     }
     const char* kb = reinterpret_cast<const char*>(a.k + krow0 + kvh * kPD);
     const char* vb = reinterpret_cast<const char*>(a.v + vrow0 + kvh * kPD);
-    char* kdst = smem + buf * 2 * kTileBytes;
     char* vdst = kdst + kTileBytes;
     const int last = nk - 1 - t0;  // rows past it are clamped to it
     const bool full = last >= kBN - 1;
@@ -189,14 +308,25 @@ void prefill_kernel(PrefillArgs a) {
   const float tau = kRescaleLog2 / c;  // threshold in score units
   const uint4 ones = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);  // bf16 1.0 pairs
 
-  if (ntiles > 0) issue_tile(0, 0);
-  for (int tile = 0; tile < ntiles; ++tile) {
+  // Tiles are issued STAGES - 1 ahead, tile t into buffer t % STAGES; loads
+  // complete in issue order, so K/V(t) has landed once at most the following
+  // tile's 2 * DU instructions are outstanding.
+  if (ntiles > 0) issue_tile(0, buffer(Buf<0>()));
+  if constexpr (STAGES > 2)
+    if (ntiles > 1) issue_tile(kBN, buffer(Buf<1>()));
+  auto step = [&](int tile, auto rb) {
+    constexpr int RB = decltype(rb)::value;
     const int t0 = tile * kBN;
-    wait_vmem();      // this wave's part of the tile has landed
-    __syncthreads();  // every wave's part has; the other buffer is free again
-    if (tile + 1 < ntiles) issue_tile(t0 + kBN, (tile + 1) & 1);
-    const char* sK = smem + (tile & 1) * 2 * kTileBytes;
+    if (STAGES > 2 && tile + 1 < ntiles) wait_vmem_le<2 * DU>(); else wait_vmem_le<0>();
+    barrier_keep_loads();  // everyone's tile is in; everyone finished tile - 1
+    if (tile + STAGES - 1 < ntiles) issue_tile(t0 + (STAGES - 1) * kBN, buffer(Buf<(RB + STAGES - 1) % STAGES>()));
+    const char* sK = buffer(rb);
     const char* sV = sK + kTileBytes;
+    // Re-define the per-lane LDS offsets at every step, so that the compiler
+    // adds them to this step's buffer here instead of keeping a hoisted
+    // address per buffer live across the loop.
+    launder(koff);
+    launder(voff);
 
     // ---- Sᵀ = K Qᵀ for both subtiles (8 independent accumulators per k-step) ----
     f32x4_t sacc[2][KT];
@@ -208,7 +338,7 @@ void prefill_kernel(PrefillArgs a) {
     for (int ks = 0; ks < 4; ++ks) {
       uint4 kop[KT];
 #pragma unroll
-      for (int kt = 0; kt < KT; ++kt) kop[kt] = *reinterpret_cast<const uint4*>(sK + k_off(kt * 16 + col, ks * 4 + g));
+      for (int kt = 0; kt < KT; ++kt) kop[kt] = *reinterpret_cast<const uint4*>(sK + kt * 16 * 256 + koff[ks]);
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) {
         sacc[0][kt] = mfma16x16x32(kop[kt], qop[0][ks], sacc[0][kt]);
@@ -234,11 +364,14 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) x[kt][i] = (kt * 16 + i <= rel) ? x[kt][i] : -INFINITY;
       }
-      float mx = fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3]));
+      // row max: this lane's scores (a chain of 3-input maxima), then the
+      // lanes holding the same query (lane ^ 16, lane ^ 32)
+      float mx = fmaxf(fmaxf(x[0][0], x[0][1]), x[0][2]);
 #pragma unroll
-      for (int kt = 1; kt < KT; ++kt) mx = fmaxf(mx, fmaxf(fmaxf(x[kt][0], x[kt][1]), fmaxf(x[kt][2], x[kt][3])));
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      for (int e = 3; e + 1 < 4 * KT; e += 2) mx = fmaxf(fmaxf(mx, x[e / 4][e % 4]), x[(e + 1) / 4][(e + 1) % 4]);
+      mx = fmaxf(mx, x[KT - 1][3]);
+      mx = max_xor16(mx);
+      mx = max_xor32(mx);
       if (__ballot(mx > m[u] + tau)) {
         const float mnew = fmaxf(m[u], mx);
         const float alpha = fast_exp2((m[u] - mnew) * c);
@@ -263,24 +396,35 @@ void prefill_kernel(PrefillArgs a) {
     }
 
     // ---- Oᵀ += Vᵀ Pᵀ, and the row sums (16 independent accumulators per k-step) ----
-    const int trow = 4 * g + (col >> 2);  // key row this lane addresses inside a 16-key half
-    const int tq = col & 3;               // which 4-dim segment
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      const int r0 = kk * 32 + trow, r1 = r0 + 16;
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const int ch = 2 * dt + (tq >> 1), half = (tq & 1) * 8;
-        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(sV + v_off(r0, ch) + half));
-        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(sV + v_off(r1, ch) + half));
-        const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
-        const uint4 vop = make_uint4(l2.x, l2.y, h2.x, h2.y);
-        oacc[0][dt] = mfma16x16x32(vop, pop[0][kk], oacc[0][dt]);
-        oacc[1][dt] = mfma16x16x32(vop, pop[1][kk], oacc[1][dt]);
+    // Read pair j = 8 kk + dt (keys 32 kk + 0..15 and 16..31, dims 16 dt ..)
+    // is issued kVWin pairs ahead of its MFMAs.
+    const uint32_t vbase = lds_addr(sV);
+    v2i_t vlo[8 * KK], vhi[8 * KK];
+    auto issue_pair = [&](auto jc) {
+      constexpr int j = decltype(jc)::value, kk = j / 8, dt = j % 8;
+      vlo[j] = ds_read_tr_b64<kk * 32 * 256>(vbase + voff[dt]);
+      vhi[j] = ds_read_tr_b64<(kk * 32 + 16) * 256>(vbase + voff[dt]);
+    };
+    static_for<kVWin>([&](auto jc) { issue_pair(jc); });
+    static_for<8 * KK>([&](auto jc) {
+      constexpr int j = decltype(jc)::value, kk = j / 8, dt = j % 8;
+      constexpr int issued = j + kVWin < 8 * KK ? j + kVWin : 8 * KK;
+      wait_lds_le<2 * (issued - j - 1)>(vlo[j], vhi[j]);
+      if constexpr (j + kVWin < 8 * KK) issue_pair(Buf<j + kVWin>());
+      const uint4 vop = make_uint4(vlo[j].x, vlo[j].y, vhi[j].x, vhi[j].y);
+      oacc[0][dt] = mfma16x16x32(vop, pop[0][kk], oacc[0][dt]);
+      oacc[1][dt] = mfma16x16x32(vop, pop[1][kk], oacc[1][dt]);
+      if constexpr (dt == 7) {
+        oacc[0][8] = mfma16x16x32(ones, pop[0][kk], oacc[0][8]);
+        oacc[1][8] = mfma16x16x32(ones, pop[1][kk], oacc[1][8]);
       }
-      oacc[0][8] = mfma16x16x32(ones, pop[0][kk], oacc[0][8]);
-      oacc[1][8] = mfma16x16x32(ones, pop[1][kk], oacc[1][8]);
-    }
+    });
+  };
+  for (int tile = 0; tile < ntiles; tile += STAGES) {
+    step(tile, Buf<0>());
+    if (tile + 1 < ntiles) step(tile + 1, Buf<1>());
+    if constexpr (STAGES > 2)
+      if (tile + 2 < ntiles) step(tile + 2, Buf<2>());
   }
 
   // ---- epilogue: normalise and write the rows that exist ----
