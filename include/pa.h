@@ -168,13 +168,18 @@ int pa_decode(void* out, const void* q, int64_t q_seq_stride, const void* k_cach
  *               block_table != NULL: the caches [num_blocks, block_size,
  *               num_kv_heads, head_dim] (the strides are then ignored), key
  *               t of sequence i at row t % block_size of block
- *               block_table[i, t / block_size].
+ *               block_table[i, t / block_size]. Token strides and
+ *               num_kv_heads * head_dim above 2^23 elements return
+ *               PA_ERR_UNSUPPORTED.
  * cu_seqlens_q, cu_seqlens_k  [num_seqs + 1] int32, non-decreasing from 0.
  * max_seqlen_q  upper bound of every nq (sizes the launch grid).
  * max_seqlen_k  upper bound of every nk; selects the key tile (32 keys up to
  *               1024, else 64). It only affects speed: results are correct
  *               for any value.
- * block_table   optional [num_seqs, max_blocks_per_seq] int32.
+ * block_table   optional [num_seqs, max_blocks_per_seq] int32; row i must
+ *               name a block for every one of sequence i's keys
+ *               (max_blocks_per_seq * block_size >= nk); entries past
+ *               max_blocks_per_seq are never read.
  */
 int pa_prefill_varlen(void* out, const void* q, int64_t q_token_stride, const void* k, const void* v,
                       int64_t k_token_stride, int64_t v_token_stride, const int32_t* cu_seqlens_q,

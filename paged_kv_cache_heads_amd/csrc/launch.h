@@ -53,6 +53,7 @@ struct PrefillArgs {
   int32_t block_size;
   int32_t num_seqs;
   int32_t num_q_tiles;
+  int64_t items_per_xcd;  // ceil(num_kv_heads * num_seqs * num_q_tiles / 8)
   int32_t max_seqlen_k;
   int32_t num_q_heads;
   int32_t num_kv_heads;

@@ -229,6 +229,8 @@ int pa_prefill_varlen(void* out, const void* q, int64_t q_token_stride, const vo
   if (st) return st;
   if (!(scale == scale) || isinf(scale)) return fail(PA_ERR_INVALID_ARGUMENT, "scale must be finite");
   const int64_t kv_row = (int64_t)num_kv_heads * head_dim;
+  if (kv_row > (int64_t)1 << 23)
+    return fail(PA_ERR_UNSUPPORTED, "num_kv_heads * head_dim above 2^23 is not supported");
   if (block_table) {
     st = check_block_size(block_size);
     if (st) return st;
@@ -241,6 +243,9 @@ int pa_prefill_varlen(void* out, const void* q, int64_t q_token_stride, const vo
                   (long long)k_token_stride, (long long)v_token_stride, (long long)kv_row);
     if (k_token_stride % 8 || v_token_stride % 8)
       return fail(PA_ERR_ALIGNMENT, "k/v token strides must be 16-byte aligned");
+    // a 64-token tile must span less than 2 GiB (32-bit offsets inside a tile)
+    if (k_token_stride > (int64_t)1 << 23 || v_token_stride > (int64_t)1 << 23)
+      return fail(PA_ERR_UNSUPPORTED, "k/v token strides above 2^23 elements are not supported");
   }
   if (num_seqs == 0 || max_seqlen_q == 0) return ok();
   if (!out || !q || !k || !v || !cu_seqlens_q || !cu_seqlens_k)
@@ -267,6 +272,9 @@ int pa_prefill_varlen(void* out, const void* q, int64_t q_token_stride, const vo
   a.block_size = block_table ? block_size : 0;
   a.num_seqs = num_seqs;
   a.num_q_tiles = (max_seqlen_q + qp - 1) / qp;
+  a.items_per_xcd = ((int64_t)num_kv_heads * num_seqs * a.num_q_tiles + 7) / 8;
+  if (a.items_per_xcd > (int64_t)INT32_MAX / 8)
+    return fail(PA_ERR_UNSUPPORTED, "num_kv_heads * num_seqs * query tiles exceeds the grid range");
   a.max_seqlen_k = max_seqlen_k;
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = num_kv_heads;

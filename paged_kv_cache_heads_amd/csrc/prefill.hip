@@ -17,8 +17,9 @@
 // an FMA, an exp and half a convert per score):
 // * One workgroup (4 waves) per (tile of 128/G query positions, kv head,
 //   sequence): it covers all G query heads of the kv head, so every K/V tile
-//   staged in LDS serves 128 query rows. Workgroups are issued heaviest first
-//   across all sequences (last query tiles, which see the most keys, first).
+//   staged in LDS serves 128 query rows. The query tiles of one (sequence,
+//   kv head) run back to back on one XCD (heaviest first), so their repeated
+//   reads of the same K/V are served by that XCD's L2.
 // * Each wave owns two 16-row subtiles (one head, 16 positions each).
 // * Scores are computed transposed, Sᵀ = K Qᵀ, with v_mfma_f32_16x16x32_bf16:
 //   K (row-major in LDS) is the A operand, Q (registers) the B operand. Each
@@ -187,9 +188,17 @@ void prefill_kernel(PrefillArgs a) {
 
   constexpr int QP = 128 / G;  // query positions per workgroup
   constexpr int PB = QP / 16;  // 16-position subtiles per head
-  const int kvh = blockIdx.x;
-  const int seq = blockIdx.y;
-  const int qtile = a.num_q_tiles - 1 - (int)blockIdx.z;
+  // Work item of this workgroup. Workgroup ids are dealt to the 8 XCDs
+  // round-robin (id % 8) and each XCD has its own L2, so XCD x takes the
+  // contiguous slice x of the items ordered by (kv head, sequence, query tile
+  // from the last): the workgroups running together on one XCD then share
+  // the K/V of a few sequences, which stays in that L2 across their query
+  // tiles, instead of streaming a different sequence's K/V per workgroup.
+  const int64_t item = (int64_t)(blockIdx.x & 7) * a.items_per_xcd + (blockIdx.x >> 3);
+  if (item >= (int64_t)a.num_kv_heads * a.num_seqs * a.num_q_tiles) return;
+  const int qtile = a.num_q_tiles - 1 - (int)(item % a.num_q_tiles);
+  const int seq = (int)((item / a.num_q_tiles) % a.num_seqs);
+  const int kvh = (int)(item / ((int64_t)a.num_q_tiles * a.num_seqs));
   const int q_beg = a.cu_seqlens_q[seq];
   const int nq = a.cu_seqlens_q[seq + 1] - q_beg;
   const int k_beg = a.cu_seqlens_k[seq];
@@ -197,7 +206,8 @@ void prefill_kernel(PrefillArgs a) {
   const int q0 = qtile * QP;
   if (q0 >= nq) return;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, g = lane >> 4;
   const int shift = nk - nq;  // causal: query j sees keys <= shift + j
 
@@ -232,24 +242,18 @@ void prefill_kernel(PrefillArgs a) {
     for (int dt = 0; dt < 9; ++dt) oacc[u][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  // Tile staging: DMA instruction n = DU * wave + u (u < DU) fills 1 KiB of
-  // the tile = rows 4n .. 4n + 3; lane i supplies row 4n + i / 16, physical
-  // chunk i % 16, i.e. the logical chunk that the swizzle maps there.
+  // Tile staging: DMA instruction u (u < DU) of wave w fills the 1 KiB of
+  // rows 16u + 4w .. 16u + 4w + 3; lane i supplies row 16u + 4w + i / 16,
+  // physical chunk i % 16, i.e. the logical chunk that the swizzle maps
+  // there. The swizzle only depends on the row mod 16, which is the same for
+  // every u, so one per-lane offset serves all instructions of a tile and the
+  // rest of each address is uniform.
   const int64_t kstride = a.block_table ? (int64_t)a.num_kv_heads * kPD : a.k_token_stride;
   const int64_t vstride = a.block_table ? (int64_t)a.num_kv_heads * kPD : a.v_token_stride;
-  int srow[DU];
-  uint32_t kofs[DU], vofs[DU];
-#pragma unroll
-  for (int u = 0; u < DU; ++u) {
-    srow[u] = 4 * (DU * wave + u) + (lane >> 4);
-    const int pc = lane & 15;
-    kofs[u] = (uint32_t)(srow[u] * kstride * 2) + ((pc ^ (srow[u] & 15)) << 4);
-    vofs[u] = (uint32_t)(srow[u] * vstride * 2) + ((pc ^ ((srow[u] & 7) << 1)) << 4);
-  }
+  const int srow0 = 4 * wave + (lane >> 4);  // row of instruction 0; + 16u for instruction u
+  const uint32_t kofs = (uint32_t)(srow0 * kstride * 2) + (((lane & 15) ^ (srow0 & 15)) << 4);
+  const uint32_t vofs = (uint32_t)(srow0 * vstride * 2) + (((lane & 15) ^ ((srow0 & 7) << 1)) << 4);
 
-  // Transposed V reads: lane L points at key row 4 g + L / 4 (of a 16-key
-  // half), 4-dim segment L % 4 of dims 16 dt ..; the swizzle only depends on
-  // the row mod 8, so the key offset of a read is an additive constant.
   // K operand reads: row kt * 16 + col, logical chunk 4 ks + g (swizzled by col).
   uint32_t koff[4];
 #pragma unroll
@@ -288,18 +292,18 @@ void prefill_kernel(PrefillArgs a) {
     const char* vb = reinterpret_cast<const char*>(a.v + vrow0 + kvh * kPD);
     char* vdst = kdst + kTileBytes;
     const int last = nk - 1 - t0;  // rows past it are clamped to it
-    const bool full = last >= kBN - 1;
 #pragma unroll
     for (int u = 0; u < DU; ++u) {
-      uint32_t ko = kofs[u], vo = vofs[u];
-      if (!full && srow[u] > last) {
-        const int pc = lane & 15;
-        ko = (uint32_t)(last * kstride * 2) + ((pc ^ (srow[u] & 15)) << 4);
-        vo = (uint32_t)(last * vstride * 2) + ((pc ^ ((srow[u] & 7) << 1)) << 4);
+      // byte offsets from the tile's first row (below 2^31: checked on the host)
+      uint32_t ko = (uint32_t)(16 * u * kstride * 2) + kofs;
+      uint32_t vo = (uint32_t)(16 * u * vstride * 2) + vofs;
+      if (last < kBN - 1 && srow0 + 16 * u > last) {
+        ko = (uint32_t)(last * kstride * 2) + (((lane & 15) ^ (srow0 & 15)) << 4);
+        vo = (uint32_t)(last * vstride * 2) + (((lane & 15) ^ ((srow0 & 7) << 1)) << 4);
       }
-      const int n = DU * wave + u;
-      __builtin_amdgcn_global_load_lds(kb + ko, (lds_void_t*)(kdst + n * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vb + vo, (lds_void_t*)(vdst + n * 1024), 16, 0, 0);
+      const int o = (16 * u + 4 * wave) * 256;
+      __builtin_amdgcn_global_load_lds(kb + ko, (lds_void_t*)(kdst + o), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vb + vo, (lds_void_t*)(vdst + o), 16, 0, 0);
     }
   };
 
@@ -446,8 +450,8 @@ void prefill_kernel(PrefillArgs a) {
 
 template <int G, int BN>
 static void launch_prefill_gb(const PrefillArgs& a, hipStream_t stream) {
-  // x: kv head, y: sequence, z: query tile counted from the last (heaviest) one
-  dim3 grid(a.num_kv_heads, a.num_seqs, a.num_q_tiles);
+  // one workgroup per work item, 8 XCD slices of items_per_xcd each
+  dim3 grid((unsigned)(8 * a.items_per_xcd));
   if (a.scale_log2e > 0.f)
     prefill_kernel<G, true, BN><<<grid, dim3(kPThreads), 0, stream>>>(a);
   else
