@@ -61,10 +61,12 @@ def prefill_flops(wl, causal=True) -> int:
 
 def measured_traffic():
     """HBM bytes per pa_decode launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
-    summary, or None if the decode kernel source changed since the counters were taken."""
+    summary, or None if the decode kernel source or the compile flags changed since the
+    counters were taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "bench_default_hbm_traffic.md")
     srcs = [os.path.join(ROOT, "paged_kv_cache_heads_amd", "csrc", n) for n in ("decode.hip", "common.h")]
+    srcs.append(os.path.join(ROOT, "paged_kv_cache_heads_amd", "build.py"))
     try:
         rec = None
         with open(path, encoding="utf-8") as f:
