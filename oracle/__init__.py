@@ -19,7 +19,13 @@ no blocking, fusion or reordering:
   "模型运行器" for the ``[num_blocks, block_size, num_kv_heads, head_dim]``
   cache), in fp64.
 
-Every function here is pinned by ``tests/test_oracle.py`` against closed forms,
+* the step before the store (``qk_norm_rope``): RMSNorm of every query and
+  key head, then the rotary embedding from a given cos/sin table (page
+  "nano-vLLM 最小化vLLM重新实现", section 6 "模型" and "辅助层"); V passes
+  through unchanged.
+
+Every function here is pinned by ``tests/test_oracle.py`` and
+``tests/test_oracle_rope.py`` against closed forms,
 invariants, a hand-worked golden example, a pure-Python brute force and
 ``torch.nn.functional.scaled_dot_product_attention``; none is "parity
 unpinned".
@@ -34,3 +40,4 @@ from .paged_attention import (  # noqa: F401
     decode,
     prefill_varlen,
 )
+from .qk_norm_rope import qk_norm_rope, rms_norm, rotate_half_pairs  # noqa: F401
