@@ -40,4 +40,4 @@ from .paged_attention import (  # noqa: F401
     decode,
     prefill_varlen,
 )
-from .qk_norm_rope import qk_norm_rope, rms_norm, rotate_half_pairs  # noqa: F401
+from .norm_rope import qk_norm_rope, rms_norm, rotate_half_pairs  # noqa: F401

@@ -1,7 +1,7 @@
 """Checks that pin the fp64 QK-norm + rotary oracle to facts other than itself.
 
 Each ``check_*`` takes a module exposing ``qk_norm_rope``, ``rms_norm`` and
-``rotate_half_pairs`` (the real ``oracle.qk_norm_rope`` or a mutant) and raises
+``rotate_half_pairs`` (the real ``oracle.norm_rope`` or a mutant) and raises
 ``AssertionError`` when the module breaks the fact. The facts: a hand-worked
 golden example (``tests/golden/qk_norm_rope_hand_worked.json``), exact
 invariants of a normalisation followed by a rotation, torch's own

@@ -5,10 +5,10 @@ import types
 
 import pytest
 
-import oracle.qk_norm_rope as orc
+import oracle.norm_rope as orc
 from tests import oracle_pins_rope as pins
 
-SRC_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "qk_norm_rope.py")
+SRC_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "norm_rope.py")
 
 MUTANTS = {
     "rotation_sign": ("a * cos - b * sin", "a * cos + b * sin"),
