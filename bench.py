@@ -6,7 +6,9 @@ One step is one pass of the whole path over seeded synthetic batches:
   prefill leg  store + causal varlen prefill over packed q/k/v (about 29 seqs
                of 100..1024 tokens, at most 16384 tokens);
   prefix leg   store + prefix-cached prefill through the block table (32 seqs
-               sharing 1024 cached tokens, 128..512 new tokens each).
+               sharing 1024 cached tokens, 128..512 new tokens each);
+  fused leg    QK-RMSNorm + rotary embedding + store of the prefill batch's
+               q/k/v (one pass, reported as its own roofline).
 Inputs are resident in HBM before timing starts. `value` is the decode leg's
 KV-read throughput (bytes of K and V the decode must read, over the leg's
 time); the prefill legs report TFLOP/s of unmasked query-key pairs. Kernel
@@ -47,6 +49,15 @@ def decode_bytes(wl) -> dict:
 def store_bytes(wl, n_tokens) -> int:
     row = wl.num_kv_heads * wl.head_dim * 2
     return n_tokens * (2 * row * 2 + 4)
+
+
+def norm_rope_bytes(wl, n_tokens) -> int:
+    """Algorithmic bytes of one fused QK-norm + rotary + store launch: the qkv row in,
+    q out, K and V rows to the cache, the position's cos/sin row, position and slot."""
+    d = wl.head_dim
+    heads = wl.num_q_heads + 2 * wl.num_kv_heads
+    per_token = heads * d * 2 * 2 + d * 4 + 4 + 4
+    return n_tokens * per_token + 2 * d * 2
 
 
 def prefill_flops(wl, causal=True) -> int:
@@ -145,8 +156,16 @@ def main():
     out3 = torch.empty((wl3.num_tokens, 16, 128), dtype=torch.bfloat16, device=dev)
     out4 = torch.empty((wl4.num_tokens, 16, 128), dtype=torch.bfloat16, device=dev)
     mq3, mq4, mk2 = wl3.max_seqlen_q, wl4.max_seqlen_q, wl2.max_context_len
+    from workloads import rope
+    nr_rng = np.random.default_rng(7)
+    nr_qw = torch.as_tensor(rope.norm_weight(nr_rng, 128).view(np.int16)).to(dev).view(torch.bfloat16)
+    nr_kw = torch.as_tensor(rope.norm_weight(nr_rng, 128).view(np.int16)).to(dev).view(torch.bfloat16)
+    nr_table = torch.as_tensor(rope.cos_sin_table(40960, 128, base=1.0e6)).to(dev)
+    nr_pos = torch.as_tensor(wl3.store_pos.astype(np.int32)).to(dev)
+    nr_q = torch.empty((wl3.num_tokens, 16, 128), dtype=torch.bfloat16, device=dev)
 
-    kernels = ["store_decode", "decode", "store_prefill", "prefill", "store_prefix", "prefill_prefix"]
+    kernels = ["store_decode", "decode", "store_prefill", "prefill", "store_prefix", "prefill_prefix",
+               "norm_rope_prefill"]
     calls = {
         "store_decode": lambda: pa.pa_store_kvcache(b2.k_new, b2.v_new, b2.k_cache, b2.v_cache, b2.slot_mapping),
         "decode": lambda: pa.pa_decode(b2.q, b2.k_cache, b2.v_cache, b2.block_tables, b2.context_lens, scale, mk2,
@@ -158,6 +177,9 @@ def main():
         "prefill_prefix": lambda: pa.pa_prefill_varlen(b4.q, b4.k_cache, b4.v_cache, b4.cu_seqlens_q,
                                                        b4.cu_seqlens_k, mq4, wl4.max_seqlen_k, scale, block_table=b4.block_tables,
                                                        out=out4),
+        "norm_rope_prefill": lambda: pa.pa_qk_norm_rope_store(b3.qkv, nr_qw, nr_kw, 1e-6, nr_table, nr_pos,
+                                                              b3.k_cache, b3.v_cache, b3.slot_mapping, 16,
+                                                              q_out=nr_q),
     }
 
     def step(events=None, i=0):
@@ -189,6 +211,7 @@ def main():
     f3, f4 = prefill_flops(wl3), prefill_flops(wl4)
     t3 = f3 / (ms["prefill"] * 1e-3) / 1e12
     t4 = f4 / (ms["prefill_prefix"] * 1e-3) / 1e12
+    nrb = norm_rope_bytes(wl3, wl3.num_tokens)
     sb = {"store_decode": store_bytes(wl2, wl2.num_seqs), "store_prefill": store_bytes(wl3, wl3.num_tokens),
           "store_prefix": store_bytes(wl4, wl4.num_tokens)}
 
@@ -226,6 +249,12 @@ def main():
                                     "achieved": round(t4, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                                     "frac": round(t4 / MFMA_BF16_PEAK_TFLOPS, 4),
                                     "avg_launch_us": round(ms["prefill_prefix"] * 1e3, 2)},
+        "roofline_norm_rope_store": {"bound": "hbm", "kernel": "norm_rope_store_kernel (varlen prefill batch)",
+                                     "achieved": round(nrb / (ms["norm_rope_prefill"] * 1e-3) / 1e9, 1),
+                                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                     "frac": round(nrb / (ms["norm_rope_prefill"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                     "bytes_per_launch": nrb,
+                                     "avg_launch_us": round(ms["norm_rope_prefill"] * 1e3, 2)},
         "kernels_us": {k: round(v * 1e3, 2) for k, v in ms.items()},
         "store_GBs": {k: round(sb[k] / (ms[k] * 1e-3) / 1e9, 1) for k in sb},
     }

@@ -91,6 +91,47 @@ int pa_store_kvcache(const void* k, int64_t k_token_stride, const void* v, int64
                      int32_t head_dim, int64_t num_blocks, int32_t block_size, void* stream);
 
 /*
+ * pa_qk_norm_rope_store — QK-RMSNorm and rotary embedding of the fused q/k/v
+ * projection output, then the KV store, in one pass.
+ *
+ * Page "nano-vLLM 最小化vLLM重新实现", section 6 "模型" and "辅助层" (RMSNorm
+ * of the q and k heads, RotaryEmbedding from a precomputed cos/sin cache) and
+ * section 5 "注意力机制" (store by slot_mapping). For token t at position
+ * p = positions[t] and each query or key head x (head_dim = 128) with weight w
+ * (q_norm_weight for query heads, k_norm_weight for key heads):
+ *   n = x / sqrt(mean(x^2) + eps) * w
+ *   y[i]      = n[i] cos_sin[p, i] - n[i + 64] cos_sin[p, 64 + i]   (i < 64)
+ *   y[i + 64] = n[i + 64] cos_sin[p, i] + n[i] cos_sin[p, 64 + i]
+ * Query heads are written to q_out; with s = slot_mapping[t] in
+ * [0, num_blocks * block_size), key heads are written to k_cache[s] and the
+ * value heads copied bit for bit to v_cache[s]. Computed in fp32 from the bf16
+ * inputs, rounded once to bf16 (round to nearest even).
+ *
+ * q_out         [num_tokens, num_q_heads, head_dim] bf16, rows
+ *               q_out_token_stride elements apart. It may be the q columns of
+ *               qkv itself (in place); any other overlap with qkv is undefined.
+ * qkv           [num_tokens, (num_q_heads + 2 num_kv_heads) * head_dim] bf16:
+ *               query heads, then key heads, then value heads; rows
+ *               qkv_token_stride elements apart.
+ * q_norm_weight, k_norm_weight  [head_dim] bf16.
+ * eps           finite, >= 0.
+ * cos_sin       [max_position, head_dim] fp32: row p holds the 64 cosines,
+ *               then the 64 sines, of position p's angles.
+ * positions     [num_tokens] int32; values outside [0, max_position) are
+ *               clamped into it.
+ * k_cache, v_cache, slot_mapping, num_blocks, block_size: as pa_store_kvcache;
+ *               tokens whose slot is negative or >= num_blocks * block_size
+ *               store nothing (their q is still written).
+ * All pointers and strides 16-byte aligned; head_dim 128; num_q_heads a
+ * multiple of num_kv_heads with group 1, 2, 4 or 8.
+ */
+int pa_qk_norm_rope_store(void* q_out, int64_t q_out_token_stride, const void* qkv, int64_t qkv_token_stride,
+                          const void* q_norm_weight, const void* k_norm_weight, float eps, const float* cos_sin,
+                          int32_t max_position, const int32_t* positions, void* k_cache, void* v_cache,
+                          const int32_t* slot_mapping, int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                          int32_t head_dim, int64_t num_blocks, int32_t block_size, void* stream);
+
+/*
  * pa_decode_workspace_size — bytes of device workspace pa_decode needs.
  *
  * Host-only and pure. split_waves is the number of waves the decode work is

@@ -16,7 +16,7 @@ from . import _lib
 from ._lib import LibraryMissing  # noqa: F401
 
 __all__ = [
-    "PAError", "LibraryMissing", "pa_store_kvcache", "pa_decode", "pa_decode_workspace_size",
+    "PAError", "LibraryMissing", "pa_store_kvcache", "pa_qk_norm_rope_store", "pa_decode", "pa_decode_workspace_size",
     "pa_decode_split_waves", "pa_prefill_varlen", "pa_status_string", "pa_last_error", "pa_version",
     "library_path",
 ]
@@ -76,6 +76,27 @@ def pa_store_kvcache(k, v, k_cache, v_cache, slot_mapping, stream=None) -> None:
     _check("pa_store_kvcache", lib.pa_store_kvcache(
         _ptr(k), _rows(k, "k"), _ptr(v), _rows(v, "v"), _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping),
         int(slot_mapping.shape[0]), hkv, d, nb, bs, _stream(stream, k_cache.device)))
+
+
+def pa_qk_norm_rope_store(qkv, q_norm_weight, k_norm_weight, eps: float, cos_sin, positions, k_cache, v_cache,
+                          slot_mapping, num_q_heads: int, q_out=None, stream=None):
+    """QK-RMSNorm + rotary embedding of qkv [T, (Hq + 2 Hkv) * D] bf16, then the KV store.
+
+    cos_sin: [max_position, D] fp32 (cosines, then sines); positions, slot_mapping: [T] int32.
+    Returns q_out [T, Hq, D] bf16 (allocated when not given; may be a view of qkv's q columns).
+    """
+    lib = _lib.load()
+    nb, bs, hkv, d = k_cache.shape
+    t = int(qkv.shape[0])
+    if qkv.dim() != 2 or qkv.stride(1) != 1:
+        raise ValueError(f"qkv must be [T, (Hq + 2 Hkv) * D] with contiguous columns, got strides {qkv.stride()}")
+    if q_out is None:
+        q_out = torch.empty((t, num_q_heads, d), dtype=torch.bfloat16, device=qkv.device)
+    _check("pa_qk_norm_rope_store", lib.pa_qk_norm_rope_store(
+        _ptr(q_out), _rows(q_out, "q_out"), _ptr(qkv), qkv.stride(0), _ptr(q_norm_weight), _ptr(k_norm_weight),
+        float(eps), _ptr(cos_sin), int(cos_sin.shape[0]), _ptr(positions), _ptr(k_cache), _ptr(v_cache),
+        _ptr(slot_mapping), t, int(num_q_heads), hkv, d, nb, bs, _stream(stream, qkv.device)))
+    return q_out
 
 
 def pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,

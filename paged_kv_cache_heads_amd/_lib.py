@@ -16,6 +16,8 @@ SIGNATURES = {
     "pa_last_error": (ctypes.c_char_p, []),
     "pa_version": (ctypes.c_int, []),
     "pa_store_kvcache": (ctypes.c_int, [_vp, _i64, _vp, _i64, _vp, _vp, _i32p, _i32, _i32, _i32, _i64, _i32, _vp]),
+    "pa_qk_norm_rope_store": (ctypes.c_int, [_vp, _i64, _vp, _i64, _vp, _vp, _f32, _vp, _i32, _i32p, _vp, _vp, _i32p,
+                                             _i32, _i32, _i32, _i32, _i64, _i32, _vp]),
     "pa_decode_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_decode_split_waves": (_i32, [_i32, _i32, _i32, _i32, _i32]),
     "pa_decode": (ctypes.c_int, [_vp, _vp, _i64, _vp, _vp, _i32p, _i32, _i32p, _i32, _i32, _i32, _i32, _i32, _i32,

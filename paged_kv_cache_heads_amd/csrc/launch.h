@@ -61,7 +61,29 @@ struct PrefillArgs {
   float scale_log2e;
 };
 
+struct NormRopeArgs {
+  uint16_t* q_out;
+  int64_t q_out_token_stride;   // elements
+  const uint16_t* qkv;
+  int64_t qkv_token_stride;     // elements
+  const uint16_t* q_weight;     // [128]
+  const uint16_t* k_weight;     // [128]
+  const float* cos_sin;         // [max_position, 128]: 64 cosines, then 64 sines
+  const int32_t* positions;
+  uint16_t* k_cache;
+  uint16_t* v_cache;
+  const int32_t* slot_mapping;
+  uint32_t num_items;           // num_tokens * (num_q_heads + 2 * num_kv_heads), below 2^31
+  int32_t num_heads;            // num_q_heads + 2 * num_kv_heads
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t max_position;
+  int32_t capacity;             // num_blocks * block_size (slots at or past it are skipped)
+  float eps;
+};
+
 hipError_t launch_store_kvcache(const StoreArgs& a, hipStream_t stream);
+hipError_t launch_norm_rope_store(const NormRopeArgs& a, hipStream_t stream);
 // group = num_q_heads / num_kv_heads (1, 2, 4 or 8); head_dim is 128.
 hipError_t launch_decode(const DecodeArgs& a, int group, hipStream_t stream);
 // Tokens per decode work chunk for a GQA group size.

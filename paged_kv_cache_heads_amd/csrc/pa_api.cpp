@@ -147,6 +147,60 @@ int pa_store_kvcache(const void* k, int64_t k_token_stride, const void* v, int64
   return hip_status(pa::launch_store_kvcache(a, static_cast<hipStream_t>(stream)), "store_kvcache launch");
 }
 
+int pa_qk_norm_rope_store(void* q_out, int64_t q_out_token_stride, const void* qkv, int64_t qkv_token_stride,
+                          const void* q_norm_weight, const void* k_norm_weight, float eps, const float* cos_sin,
+                          int32_t max_position, const int32_t* positions, void* k_cache, void* v_cache,
+                          const int32_t* slot_mapping, int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                          int32_t head_dim, int64_t num_blocks, int32_t block_size, void* stream) {
+  if (num_tokens < 0) return fail(PA_ERR_INVALID_ARGUMENT, "num_tokens %d is negative", num_tokens);
+  int st = check_heads(num_q_heads, num_kv_heads, head_dim);
+  if (st) return st;
+  if (num_blocks <= 0 || block_size <= 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "num_blocks (%lld) and block_size (%d) must be positive",
+                (long long)num_blocks, block_size);
+  if (num_blocks * (int64_t)block_size > INT32_MAX)
+    return fail(PA_ERR_UNSUPPORTED, "num_blocks * block_size exceeds the int32 slot range");
+  if (!(eps >= 0.f) || isinf(eps)) return fail(PA_ERR_INVALID_ARGUMENT, "eps must be finite and >= 0");
+  if (max_position <= 0) return fail(PA_ERR_INVALID_ARGUMENT, "max_position %d must be positive", max_position);
+  const int64_t heads = (int64_t)num_q_heads + 2 * (int64_t)num_kv_heads;
+  if (qkv_token_stride < heads * head_dim)
+    return fail(PA_ERR_INVALID_ARGUMENT, "qkv_token_stride %lld is below (num_q_heads + 2 num_kv_heads) * head_dim",
+                (long long)qkv_token_stride);
+  if (q_out_token_stride < (int64_t)num_q_heads * head_dim)
+    return fail(PA_ERR_INVALID_ARGUMENT, "q_out_token_stride %lld is below num_q_heads * head_dim",
+                (long long)q_out_token_stride);
+  if ((int64_t)num_tokens * heads >= ((int64_t)1 << 31) - 64)
+    return fail(PA_ERR_UNSUPPORTED, "num_tokens * (num_q_heads + 2 num_kv_heads) must stay below 2^31");
+  if (num_tokens == 0) return ok();
+  if (!q_out || !qkv || !q_norm_weight || !k_norm_weight || !cos_sin || !positions || !k_cache || !v_cache ||
+      !slot_mapping)
+    return fail(PA_ERR_NULL_POINTER, "every pointer argument is required");
+  if (!aligned16(q_out) || !aligned16(qkv) || !aligned16(q_norm_weight) || !aligned16(k_norm_weight) ||
+      !aligned16(cos_sin) || !aligned16(k_cache) || !aligned16(v_cache) || q_out_token_stride % 8 ||
+      qkv_token_stride % 8)
+    return fail(PA_ERR_ALIGNMENT, "pointers and token strides must be 16-byte aligned");
+  pa::NormRopeArgs a;
+  a.q_out = static_cast<uint16_t*>(q_out);
+  a.q_out_token_stride = q_out_token_stride;
+  a.qkv = static_cast<const uint16_t*>(qkv);
+  a.qkv_token_stride = qkv_token_stride;
+  a.q_weight = static_cast<const uint16_t*>(q_norm_weight);
+  a.k_weight = static_cast<const uint16_t*>(k_norm_weight);
+  a.cos_sin = cos_sin;
+  a.positions = positions;
+  a.k_cache = static_cast<uint16_t*>(k_cache);
+  a.v_cache = static_cast<uint16_t*>(v_cache);
+  a.slot_mapping = slot_mapping;
+  a.num_items = (uint32_t)(num_tokens * heads);
+  a.num_heads = (int32_t)heads;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.max_position = max_position;
+  a.capacity = (int32_t)(num_blocks * block_size);
+  a.eps = eps;
+  return hip_status(pa::launch_norm_rope_store(a, static_cast<hipStream_t>(stream)), "qk_norm_rope_store launch");
+}
+
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                 int32_t max_context_len, int32_t split_waves) {
   if (head_dim != kHeadDim) return 0;

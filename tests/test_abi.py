@@ -39,7 +39,7 @@ def declared_functions():
 
 def test_header_declares_entry_points():
     names = declared_functions()
-    for n in ["pa_store_kvcache", "pa_decode", "pa_decode_workspace_size", "pa_prefill_varlen",
+    for n in ["pa_store_kvcache", "pa_qk_norm_rope_store", "pa_decode", "pa_decode_workspace_size", "pa_prefill_varlen",
               "pa_status_string", "pa_last_error"]:
         assert n in names
 
@@ -153,3 +153,36 @@ def test_python_binding_reports_errors(lib):
     with pytest.raises(pa.PAError) as e:
         pa._check("pa_decode", INVAL)
     assert "invalid argument" in str(e.value)
+
+
+def norm_rope(lib, **kw):
+    a = dict(qo=A, qos=2048, qkv=A, qkvs=4096, qw=A, kw=A, eps=1e-6, cs=A, maxp=4096, pos=A, kc=A, vc=A, slot=A,
+             T=4, hq=16, hkv=8, d=128, nb=16, bs=256, stream=None)
+    a.update(kw)
+    return lib.pa_qk_norm_rope_store(a["qo"], a["qos"], a["qkv"], a["qkvs"], a["qw"], a["kw"], a["eps"], a["cs"],
+                                     a["maxp"], a["pos"], a["kc"], a["vc"], a["slot"], a["T"], a["hq"], a["hkv"],
+                                     a["d"], a["nb"], a["bs"], a["stream"])
+
+
+def test_norm_rope_validation(lib):
+    assert norm_rope(lib, T=-1) == INVAL
+    assert norm_rope(lib, d=64) == UNSUP
+    assert norm_rope(lib, hq=12) == INVAL
+    assert norm_rope(lib, hq=24) == UNSUP
+    assert norm_rope(lib, nb=0) == INVAL
+    assert norm_rope(lib, nb=1 << 24) == UNSUP
+    assert norm_rope(lib, eps=-1.0) == INVAL
+    assert norm_rope(lib, eps=float("nan")) == INVAL
+    assert norm_rope(lib, eps=float("inf")) == INVAL
+    assert norm_rope(lib, maxp=0) == INVAL
+    assert norm_rope(lib, qkvs=4088) == INVAL     # below 32 heads x 128
+    assert norm_rope(lib, qos=1024) == INVAL      # below 16 heads x 128
+    assert norm_rope(lib, T=1 << 27) == UNSUP     # items past 2^31
+    assert norm_rope(lib, cs=None) == NULLP
+    assert norm_rope(lib, pos=None) == NULLP
+    assert norm_rope(lib, kw=None) == NULLP
+    assert norm_rope(lib, qkv=A + 8) == ALIGN
+    assert norm_rope(lib, cs=A + 4) == ALIGN
+    assert norm_rope(lib, qkvs=4100) == ALIGN
+    assert norm_rope(lib, T=0, qo=None, qkv=None, qw=None, kw=None, cs=None, pos=None, kc=None, vc=None,
+                     slot=None) == PA_OK
