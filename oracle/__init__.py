@@ -24,8 +24,13 @@ no blocking, fusion or reordering:
   "nano-vLLM 最小化vLLM重新实现", section 6 "模型" and "辅助层"); V passes
   through unchanged.
 
-Every function here is pinned by ``tests/test_oracle.py`` and
-``tests/test_oracle_rope.py`` against closed forms,
+* the host block manager (``block_manager.BlockManager``): a pool of
+  fixed-size blocks from a free list with reference counts, chained xxh64
+  hashes of full token blocks for prefix reuse, and release on finish or
+  preemption (page "nano-vLLM 最小化vLLM重新实现", section 3 "块管理器").
+
+Every function here is pinned by ``tests/test_oracle.py``,
+``tests/test_oracle_rope.py`` and ``tests/test_oracle_blocks.py`` against closed forms,
 invariants, a hand-worked golden example, a pure-Python brute force and
 ``torch.nn.functional.scaled_dot_product_attention``; none is "parity
 unpinned".
