@@ -92,6 +92,48 @@ def measured_traffic():
     return rec["bytes_per_launch"]
 
 
+def host_block_manager(wl2, wl4, reps=20):
+    """Host timings of the C++ block manager on the bench's batches (best of reps):
+    allocating the prefix batch's 32 prompts (1024 shared tokens reused from the
+    cache after the first), one decode step for the 256-sequence batch (one batched
+    append plus its decode metadata), and XXH64 throughput over 1 MiB."""
+    from paged_kv_cache_heads_amd.blocks import BlockManager, xxh64
+
+    rng = np.random.default_rng(5)
+    prefix = rng.integers(0, 32000, 1024).tolist()
+    prompts = [np.asarray(prefix + rng.integers(0, 32000, int(n) - 1024).tolist(), dtype=np.int32)
+               for n in np.diff(wl4.cu_seqlens_k)]
+    alloc, cached = [], 0
+    for _ in range(reps):
+        bm = BlockManager(wl4.num_blocks, wl4.block_size)
+        t0 = time.perf_counter()
+        cached = sum(bm.allocate(i, p) for i, p in enumerate(prompts))
+        alloc.append(time.perf_counter() - t0)
+    bm = BlockManager(wl2.num_blocks, wl2.block_size)
+    for i, n in enumerate(wl2.context_lens):
+        bm.allocate(i, rng.integers(0, 32000, max(int(n) - 1, 0)).tolist())
+    ids = np.arange(wl2.num_seqs, dtype=np.int64)
+    width = int(wl2.block_tables.shape[1])
+    step = []
+    for r in range(reps):
+        toks = np.full(wl2.num_seqs, r, dtype=np.int32)
+        t0 = time.perf_counter()
+        bm.append_batch(ids, toks)
+        bm.decode_metadata(ids, width + 1)
+        step.append(time.perf_counter() - t0)
+    data = rng.integers(0, 256, 1 << 20, dtype=np.uint8).tobytes()
+    hs = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        xxh64(data, 0)
+        hs.append(time.perf_counter() - t0)
+    total_prompt = sum(len(p) for p in prompts)
+    return {"allocate_prefix_batch_us": round(min(alloc) * 1e6, 1), "prefix_batch_prompt_tokens": total_prompt,
+            "prefix_batch_cached_tokens": cached, "decode_step_256_seqs_us": round(min(step) * 1e6, 1),
+            "xxh64_GBs": round((1 << 20) / min(hs) / 1e9, 2), "threads": 1,
+            "note": "host C++ through the Python binding (call overhead included)"}
+
+
 def cpu_baseline(batch, wl, budget_s=15.0):
     """The fp64 oracle on a bounded prefix of the decode batch, on the host."""
     import threadpoolctl
@@ -263,6 +305,7 @@ def main():
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
+    result["host_block_manager"] = host_block_manager(wl2, wl4)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(b2, wl2)
     print(json.dumps(result), flush=True)

@@ -54,7 +54,9 @@ typedef enum pa_status {
   PA_ERR_UNSUPPORTED = 3,         /* valid but not implemented: head_dim, group size, block_size */
   PA_ERR_ALIGNMENT = 4,           /* pointer or stride not 16-byte aligned */
   PA_ERR_WORKSPACE_TOO_SMALL = 5, /* decode workspace smaller than pa_decode_workspace_size() */
-  PA_ERR_HIP = 6                  /* the HIP runtime reported an error at launch */
+  PA_ERR_HIP = 6,                 /* the HIP runtime reported an error at launch */
+  PA_ERR_NO_BLOCKS = 7,           /* block manager (pa_blocks.h): too few free blocks; nothing changed */
+  PA_ERR_NOT_FOUND = 8            /* block manager: unknown sequence id */
 } pa_status;
 
 /* Static description of a status code; never NULL. */

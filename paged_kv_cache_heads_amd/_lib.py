@@ -24,6 +24,21 @@ SIGNATURES = {
                                  _f32, _i32, _vp, _sz, _vp]),
     "pa_prefill_varlen": (ctypes.c_int, [_vp, _vp, _i64, _vp, _vp, _i64, _i64, _i32p, _i32p, _i32, _i32, _i32, _i32,
                                          _i32, _i32, _f32, _i32, _i32p, _i32, _i32, _vp]),
+    # host block manager (include/pa_blocks.h); host pointers
+    "pa_xxh64": (ctypes.c_uint64, [_vp, _sz, ctypes.c_uint64]),
+    "pa_bm_create": (ctypes.c_int, [_i32, _i32, _vp, ctypes.POINTER(_vp)]),
+    "pa_bm_destroy": (None, [_vp]),
+    "pa_bm_allocate": (ctypes.c_int, [_vp, _i64, _vp, _i32, ctypes.POINTER(_i32)]),
+    "pa_bm_append": (ctypes.c_int, [_vp, _i64, _i32]),
+    "pa_bm_append_batch": (ctypes.c_int, [_vp, _vp, _vp, _i32, ctypes.POINTER(_i32)]),
+    "pa_bm_free": (ctypes.c_int, [_vp, _i64]),
+    "pa_bm_num_free": (_i32, [_vp]),
+    "pa_bm_seq_len": (_i32, [_vp, _i64]),
+    "pa_bm_block_table": (ctypes.c_int, [_vp, _i64, _vp, _i32, ctypes.POINTER(_i32)]),
+    "pa_bm_free_list": (ctypes.c_int, [_vp, _vp, _i32, ctypes.POINTER(_i32)]),
+    "pa_bm_block_ref": (_i32, [_vp, _i32]),
+    "pa_bm_decode_metadata": (ctypes.c_int, [_vp, _vp, _i32, _i32, _vp, _vp, _vp]),
+    "pa_bm_prefill_metadata": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _i64]),
 }
 
 _LIB = None

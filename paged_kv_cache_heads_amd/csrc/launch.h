@@ -7,6 +7,11 @@
 
 namespace pa {
 
+// Record the message of a failing call (pa_last_error) and return its status;
+// ok() clears it and returns PA_OK. Defined in pa_api.cpp.
+int fail(int status, const char* fmt, ...);
+int ok();
+
 struct StoreArgs {
   const uint16_t* k;
   const uint16_t* v;

@@ -11,8 +11,10 @@
 #include "launch.h"
 
 namespace {
-
 thread_local char g_last_error[512] = "";
+}  // namespace
+
+namespace pa {
 
 int fail(int status, const char* fmt, ...) {
   va_list ap;
@@ -26,6 +28,13 @@ int ok() {
   g_last_error[0] = '\0';
   return PA_OK;
 }
+
+}  // namespace pa
+
+namespace {
+
+using pa::fail;
+using pa::ok;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -100,6 +109,8 @@ const char* pa_status_string(int status) {
     case PA_ERR_ALIGNMENT: return "misaligned pointer or stride";
     case PA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case PA_ERR_HIP: return "HIP runtime error";
+    case PA_ERR_NO_BLOCKS: return "not enough free cache blocks";
+    case PA_ERR_NOT_FOUND: return "unknown sequence";
     default: return "unknown status";
   }
 }

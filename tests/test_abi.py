@@ -16,7 +16,7 @@ import paged_kv_cache_heads_amd as pa
 from paged_kv_cache_heads_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "pa.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("pa.h", "pa_blocks.h")]
 
 PA_OK, NULLP, INVAL, UNSUP, ALIGN, WS = 0, 1, 2, 3, 4, 5
 A = 0x100000  # a 16-byte aligned fake address (never dereferenced)
@@ -31,8 +31,10 @@ def lib():
 
 
 def declared_functions():
-    with open(HEADER, encoding="utf-8") as f:
-        text = f.read()
+    text = ""
+    for h in HEADERS:
+        with open(h, encoding="utf-8") as f:
+            text += f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text)))
 
@@ -40,7 +42,8 @@ def declared_functions():
 def test_header_declares_entry_points():
     names = declared_functions()
     for n in ["pa_store_kvcache", "pa_qk_norm_rope_store", "pa_decode", "pa_decode_workspace_size", "pa_prefill_varlen",
-              "pa_status_string", "pa_last_error"]:
+              "pa_status_string", "pa_last_error", "pa_bm_create", "pa_bm_allocate", "pa_bm_append_batch",
+              "pa_bm_prefill_metadata", "pa_xxh64"]:
         assert n in names
 
 
@@ -51,7 +54,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for s in range(0, 7):
+    for s in range(0, 9):
         assert lib.pa_status_string(s)
     assert lib.pa_status_string(99) == b"unknown status"
     assert lib.pa_version() >= 100
