@@ -9,6 +9,9 @@ One step is one pass of the whole path over seeded synthetic batches:
                sharing 1024 cached tokens, 128..512 new tokens each);
   fused leg    QK-RMSNorm + rotary embedding + store of the prefill batch's
                q/k/v (one pass, reported as its own roofline).
+After the timed steps (outside them): host timings of the C++ block manager,
+and the wall-clock decode-step latency eager vs graph-captured at batch 1, 16
+and 256.
 Inputs are resident in HBM before timing starts. `value` is the decode leg's
 KV-read throughput (bytes of K and V the decode must read, over the leg's
 time); the prefill legs report TFLOP/s of unmasked query-key pairs. Kernel
@@ -132,6 +135,49 @@ def host_block_manager(wl2, wl4, reps=20):
             "prefix_batch_cached_tokens": cached, "decode_step_256_seqs_us": round(min(step) * 1e6, 1),
             "xxh64_GBs": round((1 << 20) / min(hs) / 1e9, 2), "threads": 1,
             "note": "host C++ through the Python binding (call overhead included)"}
+
+
+def decode_graph_latency(pa, torch, b2, wl2, scale, batches=(1, 16, 256), iters=200):
+    """Wall-clock time per decode step (store + decode), eager through the binding vs one
+    graph launch, for the first `batch` sequences of the decode batch (back to back on one
+    stream, synchronised once per measurement)."""
+    dev = b2.q.device
+    sizes = [1, 2, 4, 8, 16, 32, 64, 128, 256]
+    maxb = sizes[-1]
+    w = int(b2.block_tables.shape[1])
+    max_len = w * wl2.block_size
+    q_s, k_s, v_s = b2.q.clone(), b2.k_new.contiguous(), b2.v_new.contiguous()
+    slot_s, bt_s, cl_s = b2.slot_mapping.clone(), b2.block_tables.clone(), b2.context_lens.clone()
+    out_s = torch.empty_like(q_s)
+    ws = torch.empty(pa.pa_decode_workspace_size(maxb, 16, 8, 128, max_len), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.Stream()
+    res = {"batch": list(batches), "eager_step_us": [], "graph_step_us": [], "captured_sizes": sizes}
+    with torch.cuda.stream(stream):
+        graphs = pa.DecodeGraphs(q_s, k_s, v_s, slot_s, bt_s, cl_s, out_s, ws, b2.k_cache, b2.v_cache, scale,
+                                 max_len, sizes)
+        for batch in batches:
+            qs, ks, vs = q_s[:batch], k_s[:batch], v_s[:batch]
+            sl, bt, cl, o = slot_s[:batch], bt_s[:batch], cl_s[:batch], out_s[:batch]
+
+            def eager():
+                pa.pa_store_kvcache(ks, vs, b2.k_cache, b2.v_cache, sl)
+                pa.pa_decode(qs, b2.k_cache, b2.v_cache, bt, cl, scale, max_len, out=o, workspace=ws)
+
+            for fn, key in ((eager, "eager_step_us"), (lambda: graphs.launch(batch), "graph_step_us")):
+                for _ in range(10):
+                    fn()
+                stream.synchronize()
+                t0 = time.perf_counter()
+                for _ in range(iters):
+                    fn()
+                stream.synchronize()
+                res[key].append(round((time.perf_counter() - t0) / iters * 1e6, 1))
+            # the graph padded rows batch .. padded - 1 of these buffers: restore them
+            slot_s.copy_(b2.slot_mapping)
+            cl_s.copy_(b2.context_lens)
+        graphs.close()
+    stream.synchronize()
+    return res
 
 
 def cpu_baseline(batch, wl, budget_s=15.0):
@@ -306,6 +352,7 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
     result["host_block_manager"] = host_block_manager(wl2, wl4)
+    result["decode_graph"] = decode_graph_latency(pa, torch, b2, wl2, scale)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(b2, wl2)
     print(json.dumps(result), flush=True)

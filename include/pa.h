@@ -230,6 +230,72 @@ int pa_prefill_varlen(void* out, const void* q, int64_t q_token_stride, const vo
                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, float scale, int32_t causal,
                       const int32_t* block_table, int32_t max_blocks_per_seq, int32_t block_size, void* stream);
 
+/*
+ * Graph-captured decode steps (store of the new tokens + pa_decode), one HIP
+ * graph per padded batch size, replayed with a single launch (page
+ * "nano-vLLM 最小化vLLM重新实现", section 4 "模型运行器": decode graphs are
+ * captured ahead of time at batch sizes 1, 2, 4, 8, 16, 32, ..., 512 and
+ * replayed; page at bxzpzcl.cn/news/2159246, section 3.1: graphs remove the
+ * per-step launch overhead).
+ *
+ * pa_decode_step names the device buffers every captured graph reads and
+ * writes, sized for the largest batch size: row i of q, k_new, v_new,
+ * slot_mapping, block_tables, context_lens and out belongs to sequence i of the
+ * step. The caller fills rows 0 .. batch - 1 before each launch; launch sets
+ * rows batch .. padded - 1 to slot -1 and length 0 (nothing stored, zero
+ * output rows). max_context_len bounds every context length of every launch;
+ * workspace must hold pa_decode_workspace_size() for the largest batch size.
+ * The buffers must stay allocated, and the struct's values fixed, while the
+ * graphs exist.
+ */
+typedef struct pa_decode_step {
+  void* q;                    /* [max_batch, num_q_heads, head_dim] bf16 */
+  int64_t q_seq_stride;
+  const void* k_new;          /* [max_batch, num_kv_heads, head_dim] bf16 */
+  int64_t k_token_stride;
+  const void* v_new;
+  int64_t v_token_stride;
+  int32_t* slot_mapping;      /* [max_batch] */
+  const int32_t* block_tables; /* [max_batch, max_blocks_per_seq] */
+  int32_t max_blocks_per_seq;
+  int32_t* context_lens;      /* [max_batch] */
+  void* out;                  /* [max_batch, num_q_heads, head_dim] bf16 */
+  void* workspace;
+  size_t workspace_bytes;
+  void* k_cache;
+  void* v_cache;
+  int64_t num_blocks;
+  int32_t block_size;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  float scale;
+  int32_t max_context_len;
+  int32_t split_waves;
+} pa_decode_step;
+
+typedef struct pa_decode_graphs pa_decode_graphs;
+
+/*
+ * Capture one graph per entry of batch_sizes (positive, strictly increasing,
+ * at most 32 of them) on stream, which must not be the legacy default stream.
+ * Each graph is pa_store_kvcache + pa_decode at that batch size with the
+ * step's arguments; capturing launches nothing. Errors of the captured calls
+ * are returned as they are (and nothing is kept); a failed capture returns
+ * PA_ERR_HIP.
+ */
+int pa_decode_graphs_create(const pa_decode_step* step, const int32_t* batch_sizes, int32_t count, void* stream,
+                            pa_decode_graphs** out);
+
+/*
+ * One decode step of batch sequences (1 <= batch <= the largest captured
+ * size): pads rows batch .. padded - 1 and launches the graph of the smallest
+ * captured size padded >= batch on stream. *padded (optional) receives it.
+ */
+int pa_decode_graphs_launch(pa_decode_graphs* graphs, int32_t batch, void* stream, int32_t* padded);
+
+void pa_decode_graphs_destroy(pa_decode_graphs* graphs);
+
 #ifdef __cplusplus
 }
 #endif

@@ -18,7 +18,7 @@ from ._lib import LibraryMissing  # noqa: F401
 __all__ = [
     "PAError", "LibraryMissing", "pa_store_kvcache", "pa_qk_norm_rope_store", "pa_decode", "pa_decode_workspace_size",
     "pa_decode_split_waves", "pa_prefill_varlen", "pa_status_string", "pa_last_error", "pa_version",
-    "library_path",
+    "library_path", "DecodeGraphs",
 ]
 
 
@@ -156,3 +156,56 @@ def pa_prefill_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, ma
         1 if causal else 0,
         _ptr(block_table), width, bs, _stream(stream, q.device)))
     return out
+
+
+class DecodeGraphs:
+    """Graph-captured decode steps (pa_decode_graphs_*): store + decode captured once per batch size.
+
+    The tensors are the step's fixed device buffers, sized for max(batch_sizes): q [B, Hq, D],
+    k_new / v_new [B, Hkv, D] views, slot_mapping [B], block_tables [B, W], context_lens [B] (int32),
+    out [B, Hq, D], workspace (uint8, >= pa_decode_workspace_size for the largest batch). Fill rows
+    0 .. batch - 1, then launch(batch); rows past batch are padded by the library.
+    Capture needs a stream other than the legacy default stream (stream or the current torch stream).
+    """
+
+    def __init__(self, q, k_new, v_new, slot_mapping, block_tables, context_lens, out, workspace, k_cache,
+                 v_cache, scale: float, max_context_len: int, batch_sizes, split_waves: int = 0, stream=None):
+        import ctypes
+
+        lib = _lib.load()
+        self._lib = lib
+        nb, bs, hkv, d = k_cache.shape
+        self._keep = (q, k_new, v_new, slot_mapping, block_tables, context_lens, out, workspace, k_cache, v_cache)
+        st = _lib.DecodeStep(
+            q=_ptr(q), q_seq_stride=_rows(q, "q"), k_new=_ptr(k_new), k_token_stride=_rows(k_new, "k_new"),
+            v_new=_ptr(v_new), v_token_stride=_rows(v_new, "v_new"), slot_mapping=_ptr(slot_mapping),
+            block_tables=_ptr(block_tables), max_blocks_per_seq=int(block_tables.shape[1]),
+            context_lens=_ptr(context_lens), out=_ptr(out), workspace=_ptr(workspace),
+            workspace_bytes=workspace.numel() * workspace.element_size(), k_cache=_ptr(k_cache),
+            v_cache=_ptr(v_cache), num_blocks=nb, block_size=bs, num_q_heads=int(q.shape[1]), num_kv_heads=hkv,
+            head_dim=d, scale=float(scale), max_context_len=int(max_context_len), split_waves=int(split_waves))
+        sizes = (ctypes.c_int32 * len(batch_sizes))(*[int(b) for b in batch_sizes])
+        h = ctypes.c_void_p()
+        _check("pa_decode_graphs_create", lib.pa_decode_graphs_create(
+            ctypes.byref(st), sizes, len(batch_sizes), _stream(stream, q.device), ctypes.byref(h)))
+        self._h = h
+        self.batch_sizes = [int(b) for b in batch_sizes]
+        self.device = q.device
+
+    def launch(self, batch: int, stream=None) -> int:
+        """One decode step of `batch` sequences; returns the padded batch size replayed."""
+        import ctypes
+
+        padded = ctypes.c_int32(0)
+        _check("pa_decode_graphs_launch", self._lib.pa_decode_graphs_launch(
+            self._h, int(batch), _stream(stream, self.device), ctypes.byref(padded)))
+        return padded.value
+
+    def close(self) -> None:
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            self._lib.pa_decode_graphs_destroy(h)
+        self._h = None
+
+    def __del__(self):
+        self.close()

@@ -11,6 +11,18 @@ LIB_PATH = os.path.join(HERE, "libpa.so")
 _i32, _i64, _vp, _sz, _f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_float
 _i32p = ctypes.c_void_p  # int32 device pointers travel as addresses
 
+class DecodeStep(ctypes.Structure):
+    """pa_decode_step of include/pa.h (same field order and types)."""
+    _fields_ = [
+        ("q", _vp), ("q_seq_stride", _i64), ("k_new", _vp), ("k_token_stride", _i64), ("v_new", _vp),
+        ("v_token_stride", _i64), ("slot_mapping", _vp), ("block_tables", _vp), ("max_blocks_per_seq", _i32),
+        ("context_lens", _vp), ("out", _vp), ("workspace", _vp), ("workspace_bytes", _sz), ("k_cache", _vp),
+        ("v_cache", _vp), ("num_blocks", _i64), ("block_size", _i32), ("num_q_heads", _i32),
+        ("num_kv_heads", _i32), ("head_dim", _i32), ("scale", _f32), ("max_context_len", _i32),
+        ("split_waves", _i32),
+    ]
+
+
 SIGNATURES = {
     "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "pa_last_error": (ctypes.c_char_p, []),
@@ -24,6 +36,9 @@ SIGNATURES = {
                                  _f32, _i32, _vp, _sz, _vp]),
     "pa_prefill_varlen": (ctypes.c_int, [_vp, _vp, _i64, _vp, _vp, _i64, _i64, _i32p, _i32p, _i32, _i32, _i32, _i32,
                                          _i32, _i32, _f32, _i32, _i32p, _i32, _i32, _vp]),
+    "pa_decode_graphs_create": (ctypes.c_int, [ctypes.POINTER(DecodeStep), _vp, _i32, _vp, ctypes.POINTER(_vp)]),
+    "pa_decode_graphs_launch": (ctypes.c_int, [_vp, _i32, _vp, ctypes.POINTER(_i32)]),
+    "pa_decode_graphs_destroy": (None, [_vp]),
     # host block manager (include/pa_blocks.h); host pointers
     "pa_xxh64": (ctypes.c_uint64, [_vp, _sz, ctypes.c_uint64]),
     "pa_bm_create": (ctypes.c_int, [_i32, _i32, _vp, ctypes.POINTER(_vp)]),

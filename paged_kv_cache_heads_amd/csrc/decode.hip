@@ -514,6 +514,23 @@ static hipError_t launch_decode_g(const DecodeArgs& a, hipStream_t stream) {
 
 int decode_chunk_tokens(int group) { return group <= 2 ? 32 : 16; }
 
+__global__ void pad_decode_rows_kernel(int32_t* slot_mapping, int32_t* context_lens, int32_t from, int32_t to) {
+  const int32_t i = from + (int32_t)(blockIdx.x * blockDim.x + threadIdx.x);
+  if (i < to) {
+    slot_mapping[i] = -1;
+    context_lens[i] = 0;
+  }
+}
+
+hipError_t launch_pad_decode_rows(int32_t* slot_mapping, int32_t* context_lens, int32_t from, int32_t to,
+                                  hipStream_t stream) {
+  if (to <= from) return hipSuccess;
+  const int32_t n = to - from;
+  pad_decode_rows_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream>>>(slot_mapping, context_lens,
+                                                                                      from, to);
+  return hipGetLastError();
+}
+
 hipError_t launch_decode(const DecodeArgs& a, int group, hipStream_t stream) {
   if (a.num_seqs == 0) return hipSuccess;
   switch (group) {

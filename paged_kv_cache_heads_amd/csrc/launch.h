@@ -91,6 +91,9 @@ hipError_t launch_store_kvcache(const StoreArgs& a, hipStream_t stream);
 hipError_t launch_norm_rope_store(const NormRopeArgs& a, hipStream_t stream);
 // group = num_q_heads / num_kv_heads (1, 2, 4 or 8); head_dim is 128.
 hipError_t launch_decode(const DecodeArgs& a, int group, hipStream_t stream);
+// Rows [from, to) of a padded decode batch: slot -1 (store nothing), length 0 (zero output).
+hipError_t launch_pad_decode_rows(int32_t* slot_mapping, int32_t* context_lens, int32_t from, int32_t to,
+                                  hipStream_t stream);
 // Tokens per decode work chunk for a GQA group size.
 int decode_chunk_tokens(int group);
 hipError_t launch_prefill(const PrefillArgs& a, int group, hipStream_t stream);

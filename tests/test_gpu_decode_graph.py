@@ -1,0 +1,112 @@
+"""Graph-captured decode steps (pa_decode_graphs_*) against the eager step and the oracle.
+
+Graphs are captured once for batch sizes 1, 2, 4, ..., 512 over fixed buffers.
+For several real batch sizes the first rows are filled (ordinary eager work),
+the graph of the next size up is replayed, and the output must equal, bit for
+bit, the eager store + decode launched at the same padded size (the work split
+depends on the launch size); the padded rows must come out zero. Every size is replayed several times with eager work and
+synchronisation in between, each replay checked. One case is also checked
+against the oracle.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_heads_amd as pa
+from tests.gpu_common import announce, dev  # noqa: F401
+from tests.parity import Compact, assert_attention_close
+from workloads import configs, tensors
+
+pytestmark = pytest.mark.gpu
+
+SIZES = [1, 2, 4, 8, 16, 32, 64, 128, 256, 512]
+
+
+def test_decode_graphs_match_eager_and_oracle(dev):
+    announce("decode graphs 1..512 vs eager")
+    wl = configs.config2()  # 256 sequences, L ~ U{100..2048}
+    b = tensors.materialize(wl, dev)
+    scale = 1.0 / math.sqrt(128)
+    w = int(b.block_tables.shape[1])
+    maxb = SIZES[-1]
+    max_len = w * wl.block_size
+    # the step's fixed buffers (rows past the real batch are padding)
+    q_s = torch.zeros((maxb, 16, 128), dtype=torch.bfloat16, device=dev)
+    k_s = torch.zeros((maxb, 8, 128), dtype=torch.bfloat16, device=dev)
+    v_s = torch.zeros((maxb, 8, 128), dtype=torch.bfloat16, device=dev)
+    slot_s = torch.full((maxb,), -1, dtype=torch.int32, device=dev)
+    bt_s = torch.full((maxb, w), -1, dtype=torch.int32, device=dev)
+    cl_s = torch.zeros((maxb,), dtype=torch.int32, device=dev)
+    out_s = torch.empty((maxb, 16, 128), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(pa.pa_decode_workspace_size(maxb, 16, 8, 128, max_len), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        graphs = pa.DecodeGraphs(q_s, k_s, v_s, slot_s, bt_s, cl_s, out_s, ws, b.k_cache, b.v_cache, scale,
+                                 max_len, SIZES)
+        ws_e = torch.empty(pa.pa_decode_workspace_size(maxb, 16, 8, 128, max_len), dtype=torch.uint8, device=dev)
+        checked_oracle = False
+        for batch in (1, 3, 17, 100, 255, 256):
+            rows = torch.arange(batch, device=dev)
+            for rep in range(3):
+                # eager work between replays: fill the step's rows
+                q_s[:batch] = b.q[rows]
+                k_s[:batch] = b.k_new[rows]
+                v_s[:batch] = b.v_new[rows]
+                slot_s[:batch] = b.slot_mapping[rows]
+                bt_s[:batch] = b.block_tables[rows]
+                cl_s[:batch] = b.context_lens[rows]
+                out_s.fill_(1.0)
+                padded = graphs.launch(batch)
+                stream.synchronize()
+                assert padded == min(s for s in SIZES if s >= batch)
+                got = out_s[:batch].clone()
+                assert torch.all(out_s[batch:padded].float() == 0)
+                assert torch.all(slot_s[batch:padded] == -1) and torch.all(cl_s[batch:padded] == 0)
+                # the eager step over the same padded rows (same launch size, hence the same work split)
+                pa.pa_store_kvcache(k_s[:padded], v_s[:padded], b.k_cache, b.v_cache, slot_s[:padded])
+                ref = pa.pa_decode(q_s[:padded], b.k_cache, b.v_cache, bt_s[:padded], cl_s[:padded], scale,
+                                   max_len, workspace=ws_e)
+                stream.synchronize()
+                assert torch.equal(got.view(torch.int16), ref[:batch].view(torch.int16)), (batch, rep)
+            if batch == 17 and not checked_oracle:
+                seqs = list(range(batch))
+                host = Compact(b, seqs)
+                want = oracle.decode(tensors.to_u16(b.q[:batch]), host.k, host.v, host.tables,
+                                     wl.context_lens[:batch], scale)
+                assert_attention_close(got, want, "graph decode, 17 sequences")
+                checked_oracle = True
+        graphs.close()
+
+
+def test_decode_graphs_reject_bad_arguments(dev):
+    announce("decode graphs argument errors")
+    wl = configs.config1()
+    b = tensors.materialize(wl, dev)
+    maxb = 4
+    w = int(b.block_tables.shape[1])
+    bufs = [torch.zeros((maxb, 16, 128), dtype=torch.bfloat16, device=dev),
+            torch.zeros((maxb, 8, 128), dtype=torch.bfloat16, device=dev),
+            torch.zeros((maxb, 8, 128), dtype=torch.bfloat16, device=dev),
+            torch.full((maxb,), -1, dtype=torch.int32, device=dev),
+            torch.full((maxb, w), -1, dtype=torch.int32, device=dev),
+            torch.zeros((maxb,), dtype=torch.int32, device=dev),
+            torch.empty((maxb, 16, 128), dtype=torch.bfloat16, device=dev)]
+    small_ws = torch.empty(16, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        with pytest.raises(pa.PAError):  # not increasing
+            pa.DecodeGraphs(*bufs, small_ws, b.k_cache, b.v_cache, 0.1, w * 256, [2, 2])
+        with pytest.raises(pa.PAError) as e:  # workspace too small: the captured decode's own status
+            pa.DecodeGraphs(*bufs, small_ws, b.k_cache, b.v_cache, 0.1, w * 256, [1, 4])
+        assert e.value.status == 5
+        ws = torch.empty(pa.pa_decode_workspace_size(maxb, 16, 8, 128, w * 256), dtype=torch.uint8, device=dev)
+        g = pa.DecodeGraphs(*bufs, ws, b.k_cache, b.v_cache, 0.1, w * 256, [1, 4])
+        with pytest.raises(pa.PAError):
+            g.launch(5)
+        with pytest.raises(pa.PAError):
+            g.launch(0)
+        g.close()
