@@ -29,8 +29,13 @@ no blocking, fusion or reordering:
   hashes of full token blocks for prefix reuse, and release on finish or
   preemption (page "nano-vLLM 最小化vLLM重新实现", section 3 "块管理器").
 
+* the Gumbel-max sampler (``sampler.sample``): argmax of softmax(l / T) over
+  exponential noise drawn with Philox4x64-10 (page "nano-vLLM
+  最小化vLLM重新实现", "辅助层" and "关键设计选择").
+
 Every function here is pinned by ``tests/test_oracle.py``,
-``tests/test_oracle_rope.py`` and ``tests/test_oracle_blocks.py`` against closed forms,
+``tests/test_oracle_rope.py``, ``tests/test_oracle_blocks.py`` and
+``tests/test_oracle_sampler.py`` against closed forms,
 invariants, a hand-worked golden example, a pure-Python brute force and
 ``torch.nn.functional.scaled_dot_product_attention``; none is "parity
 unpinned".
