@@ -8,7 +8,9 @@ One step is one pass of the whole path over seeded synthetic batches:
   prefix leg   store + prefix-cached prefill through the block table (32 seqs
                sharing 1024 cached tokens, 128..512 new tokens each);
   fused leg    QK-RMSNorm + rotary embedding + store of the prefill batch's
-               q/k/v (one pass, reported as its own roofline).
+               q/k/v (one pass, reported as its own roofline);
+  sampler leg  Gumbel-max sampling of one token for each of the 256 decode
+               sequences over a 151936-token vocabulary (fp32 logits).
 After the timed steps (outside them): host timings of the C++ block manager,
 and the wall-clock decode-step latency eager vs graph-captured at batch 1, 16
 and 256.
@@ -36,6 +38,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "paged decode attn KV-read GB/s (% HBM peak); prefill attn TFLOP/s (% MFMA)"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+SAMPLER_VOCAB = 151936          # vocabulary of the Qwen3 family the pages benchmark
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 
 
@@ -251,9 +254,16 @@ def main():
     nr_table = torch.as_tensor(rope.cos_sin_table(40960, 128, base=1.0e6)).to(dev)
     nr_pos = torch.as_tensor(wl3.store_pos.astype(np.int32)).to(dev)
     nr_q = torch.empty((wl3.num_tokens, 16, 128), dtype=torch.bfloat16, device=dev)
+    # sampler: one token per decode sequence over a 151936-token vocabulary (fp32 logits, N(0, 2^2))
+    smp_gen = torch.Generator(device=dev)
+    smp_gen.manual_seed(9)
+    smp_logits = torch.randn((wl2.num_seqs, SAMPLER_VOCAB), generator=smp_gen, device=dev) * 2.0
+    smp_temps = torch.full((wl2.num_seqs,), 0.8, dtype=torch.float32, device=dev)
+    smp_tokens = torch.empty(wl2.num_seqs, dtype=torch.int32, device=dev)
+    smp_ws = torch.empty(pa.pa_sample_workspace_size(wl2.num_seqs, SAMPLER_VOCAB), dtype=torch.uint8, device=dev)
 
     kernels = ["store_decode", "decode", "store_prefill", "prefill", "store_prefix", "prefill_prefix",
-               "norm_rope_prefill"]
+               "norm_rope_prefill", "sample_decode"]
     calls = {
         "store_decode": lambda: pa.pa_store_kvcache(b2.k_new, b2.v_new, b2.k_cache, b2.v_cache, b2.slot_mapping),
         "decode": lambda: pa.pa_decode(b2.q, b2.k_cache, b2.v_cache, b2.block_tables, b2.context_lens, scale, mk2,
@@ -268,6 +278,8 @@ def main():
         "norm_rope_prefill": lambda: pa.pa_qk_norm_rope_store(b3.qkv, nr_qw, nr_kw, 1e-6, nr_table, nr_pos,
                                                               b3.k_cache, b3.v_cache, b3.slot_mapping, 16,
                                                               q_out=nr_q),
+        "sample_decode": lambda: pa.pa_sample_gumbel(smp_logits, smp_temps, 1234, 0, tokens=smp_tokens,
+                                                     workspace=smp_ws),
     }
 
     def step(events=None, i=0):
@@ -300,6 +312,7 @@ def main():
     t3 = f3 / (ms["prefill"] * 1e-3) / 1e12
     t4 = f4 / (ms["prefill_prefix"] * 1e-3) / 1e12
     nrb = norm_rope_bytes(wl3, wl3.num_tokens)
+    smp_bytes = wl2.num_seqs * (SAMPLER_VOCAB * 4 + 4 + 4)
     sb = {"store_decode": store_bytes(wl2, wl2.num_seqs), "store_prefill": store_bytes(wl3, wl3.num_tokens),
           "store_prefix": store_bytes(wl4, wl4.num_tokens)}
 
@@ -343,6 +356,11 @@ def main():
                                      "frac": round(nrb / (ms["norm_rope_prefill"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                                      "bytes_per_launch": nrb,
                                      "avg_launch_us": round(ms["norm_rope_prefill"] * 1e3, 2)},
+        "roofline_sampler": {"bound": "hbm", "kernel": "sample_partial + sample_final (256 x 151936 fp32 logits)",
+                             "achieved": round(smp_bytes / (ms["sample_decode"] * 1e-3) / 1e9, 1),
+                             "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": round(smp_bytes / (ms["sample_decode"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                             "bytes_per_launch": smp_bytes, "avg_launch_us": round(ms["sample_decode"] * 1e3, 2)},
         "kernels_us": {k: round(v * 1e3, 2) for k, v in ms.items()},
         "store_GBs": {k: round(sb[k] / (ms[k] * 1e-3) / 1e9, 1) for k in sb},
     }

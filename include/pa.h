@@ -231,6 +231,37 @@ int pa_prefill_varlen(void* out, const void* q, int64_t q_token_stride, const vo
                       const int32_t* block_table, int32_t max_blocks_per_seq, int32_t block_size, void* stream);
 
 /*
+ * pa_sample_gumbel — one token per row by the Gumbel-max trick.
+ *
+ * Page "nano-vLLM 最小化vLLM重新实现", "辅助层" (the sampler: exponential
+ * noise, then an argmax) and "关键设计选择" (temperature > 1e-10, no greedy
+ * sampling). For row b with logits l (vocab_size of them) and temperature
+ * T = max(temperatures[b], 1e-10):
+ *   tokens[b] = argmax_i softmax(l / T)_i / E_i,  E_i = -ln(u_i),
+ * which draws token i with probability softmax(l / T)_i. u_i comes from
+ * Philox4x64-10 (Salmon et al., SC 2011) under key (seed, 0): element i takes
+ * a 23-bit field w of 64-bit word (i / 2) % 4 of the block at counter
+ * (i / 8, b, offset, 0) -- bits 63..41 for even i, 40..18 for odd i -- and
+ * u = (w + 1/2) / 2^23. Pass a new offset (e.g. the step number) for new
+ * noise. The decision is taken in fp32 (l log2(e) / T - log2(-log2(u))); ties
+ * go to the lowest index; -inf logits are never drawn unless a whole row is
+ * -inf (then token 0 by the tie rule); NaN logits give an unspecified token in
+ * [0, vocab_size).
+ *
+ * tokens        [num_rows] int32 (device).
+ * logits        [num_rows, vocab_size] fp32, rows logits_row_stride elements
+ *               apart (>= vocab_size; rows starting 16-byte aligned are read
+ *               with 16-byte loads).
+ * temperatures  [num_rows] fp32.
+ * workspace     >= pa_sample_workspace_size(num_rows, vocab_size) bytes,
+ *               16-byte aligned, owned by the caller.
+ */
+size_t pa_sample_workspace_size(int32_t num_rows, int32_t vocab_size);
+int pa_sample_gumbel(int32_t* tokens, const float* logits, int64_t logits_row_stride, const float* temperatures,
+                     int32_t num_rows, int32_t vocab_size, uint64_t seed, uint64_t offset, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/*
  * Graph-captured decode steps (store of the new tokens + pa_decode), one HIP
  * graph per padded batch size, replayed with a single launch (page
  * "nano-vLLM 最小化vLLM重新实现", section 4 "模型运行器": decode graphs are

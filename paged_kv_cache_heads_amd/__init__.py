@@ -18,7 +18,7 @@ from ._lib import LibraryMissing  # noqa: F401
 __all__ = [
     "PAError", "LibraryMissing", "pa_store_kvcache", "pa_qk_norm_rope_store", "pa_decode", "pa_decode_workspace_size",
     "pa_decode_split_waves", "pa_prefill_varlen", "pa_status_string", "pa_last_error", "pa_version",
-    "library_path", "DecodeGraphs",
+    "library_path", "DecodeGraphs", "pa_sample_gumbel", "pa_sample_workspace_size",
 ]
 
 
@@ -97,6 +97,28 @@ def pa_qk_norm_rope_store(qkv, q_norm_weight, k_norm_weight, eps: float, cos_sin
         float(eps), _ptr(cos_sin), int(cos_sin.shape[0]), _ptr(positions), _ptr(k_cache), _ptr(v_cache),
         _ptr(slot_mapping), t, int(num_q_heads), hkv, d, nb, bs, _stream(stream, qkv.device)))
     return q_out
+
+
+def pa_sample_workspace_size(num_rows: int, vocab_size: int) -> int:
+    return int(_lib.load().pa_sample_workspace_size(num_rows, vocab_size))
+
+
+def pa_sample_gumbel(logits, temperatures, seed: int, offset: int, tokens=None, workspace=None, stream=None):
+    """One token per row of logits [B, V] fp32 (temperatures [B] fp32): int32 [B]."""
+    lib = _lib.load()
+    b, v = int(logits.shape[0]), int(logits.shape[1])
+    if logits.dim() != 2 or logits.stride(1) != 1:
+        raise ValueError("logits must be [rows, vocab] with contiguous rows")
+    if tokens is None:
+        tokens = torch.empty(b, dtype=torch.int32, device=logits.device)
+    need = lib.pa_sample_workspace_size(b, v)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=logits.device)
+    _check("pa_sample_gumbel", lib.pa_sample_gumbel(
+        _ptr(tokens), _ptr(logits), logits.stride(0), _ptr(temperatures), b, v, int(seed) & (2 ** 64 - 1),
+        int(offset) & (2 ** 64 - 1), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream, logits.device)))
+    return tokens
 
 
 def pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,

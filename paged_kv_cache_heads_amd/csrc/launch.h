@@ -87,6 +87,24 @@ struct NormRopeArgs {
   float eps;
 };
 
+struct SampleArgs {
+  int32_t* tokens;             // [num_rows]
+  const float* logits;         // [num_rows, row_stride]
+  int64_t row_stride;          // elements
+  const float* temperatures;   // [num_rows]
+  float* ws_score;             // [num_rows, chunks] per-chunk best score
+  int32_t* ws_index;           // [num_rows, chunks] and its index
+  uint64_t seed;
+  uint64_t offset;
+  int32_t num_rows;
+  int32_t vocab;
+  int32_t chunks;              // sample_chunks(vocab)
+};
+
+// Vocabulary chunks (one workgroup each) per row of the sampler.
+int32_t sample_chunks(int32_t vocab);
+hipError_t launch_sample(const SampleArgs& a, hipStream_t stream);
+
 hipError_t launch_store_kvcache(const StoreArgs& a, hipStream_t stream);
 hipError_t launch_norm_rope_store(const NormRopeArgs& a, hipStream_t stream);
 // group = num_q_heads / num_kv_heads (1, 2, 4 or 8); head_dim is 128.

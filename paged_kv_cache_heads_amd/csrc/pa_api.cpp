@@ -212,6 +212,45 @@ int pa_qk_norm_rope_store(void* q_out, int64_t q_out_token_stride, const void* q
   return hip_status(pa::launch_norm_rope_store(a, static_cast<hipStream_t>(stream)), "qk_norm_rope_store launch");
 }
 
+size_t pa_sample_workspace_size(int32_t num_rows, int32_t vocab_size) {
+  if (num_rows < 0 || vocab_size <= 0) return 0;
+  return (size_t)num_rows * (size_t)pa::sample_chunks(vocab_size) * (sizeof(float) + sizeof(int32_t));
+}
+
+int pa_sample_gumbel(int32_t* tokens, const float* logits, int64_t logits_row_stride, const float* temperatures,
+                     int32_t num_rows, int32_t vocab_size, uint64_t seed, uint64_t offset, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  if (num_rows < 0 || vocab_size <= 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "num_rows (%d) must be >= 0 and vocab_size (%d) positive", num_rows,
+                vocab_size);
+  if (num_rows > 65535) return fail(PA_ERR_UNSUPPORTED, "num_rows %d exceeds 65535", num_rows);
+  if (logits_row_stride < vocab_size)
+    return fail(PA_ERR_INVALID_ARGUMENT, "logits_row_stride %lld is below vocab_size %d",
+                (long long)logits_row_stride, vocab_size);
+  if (num_rows == 0) return ok();
+  if (!tokens || !logits || !temperatures || !workspace)
+    return fail(PA_ERR_NULL_POINTER, "tokens, logits, temperatures and workspace are required");
+  if ((reinterpret_cast<uintptr_t>(logits) & 3u) || !aligned16(workspace))
+    return fail(PA_ERR_ALIGNMENT, "logits must be 4-byte and the workspace 16-byte aligned");
+  const size_t need = pa_sample_workspace_size(num_rows, vocab_size);
+  if (workspace_bytes < need)
+    return fail(PA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < required %zu", workspace_bytes, need);
+  pa::SampleArgs a;
+  a.tokens = tokens;
+  a.logits = logits;
+  a.row_stride = logits_row_stride;
+  a.temperatures = temperatures;
+  a.chunks = pa::sample_chunks(vocab_size);
+  a.ws_score = static_cast<float*>(workspace);
+  a.ws_index = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
+                                          (size_t)num_rows * a.chunks * sizeof(float));
+  a.seed = seed;
+  a.offset = offset;
+  a.num_rows = num_rows;
+  a.vocab = vocab_size;
+  return hip_status(pa::launch_sample(a, static_cast<hipStream_t>(stream)), "sample launch");
+}
+
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                 int32_t max_context_len, int32_t split_waves) {
   if (head_dim != kHeadDim) return 0;

@@ -189,3 +189,24 @@ def test_norm_rope_validation(lib):
     assert norm_rope(lib, qkvs=4100) == ALIGN
     assert norm_rope(lib, T=0, qo=None, qkv=None, qw=None, kw=None, cs=None, pos=None, kc=None, vc=None,
                      slot=None) == PA_OK
+
+
+def test_sampler_validation(lib):
+    def smp(**kw):
+        a = dict(tok=A, lg=A, ls=1024, t=A, B=4, V=1000, seed=1, off=0, ws=A, wsb=1 << 20, stream=None)
+        a.update(kw)
+        return lib.pa_sample_gumbel(a["tok"], a["lg"], a["ls"], a["t"], a["B"], a["V"], a["seed"], a["off"],
+                                    a["ws"], a["wsb"], a["stream"])
+    assert lib.pa_sample_workspace_size(4, 1000) == 4 * 1 * 8
+    assert lib.pa_sample_workspace_size(2, 151936) == 2 * 19 * 8
+    assert lib.pa_sample_workspace_size(2, 0) == 0
+    assert smp(B=-1) == INVAL
+    assert smp(V=0) == INVAL
+    assert smp(ls=999) == INVAL
+    assert smp(B=70000) == UNSUP
+    assert smp(lg=None) == NULLP
+    assert smp(ws=None) == NULLP
+    assert smp(lg=A + 2) == ALIGN
+    assert smp(ws=A + 4) == ALIGN
+    assert smp(wsb=8) == WS
+    assert smp(B=0, tok=None, lg=None, t=None, ws=None) == PA_OK
