@@ -218,6 +218,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--split-waves", type=int, default=0, help="decode work split (0 = library choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--step-only", action="store_true",
+                    help="skip the untimed host block-manager and decode-graph legs (profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, run one 256 MiB device copy (reads and writes a known byte count) "
                          "so that profiler byte counters can be calibrated against it")
@@ -369,8 +371,9 @@ def main():
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
-    result["host_block_manager"] = host_block_manager(wl2, wl4)
-    result["decode_graph"] = decode_graph_latency(pa, torch, b2, wl2, scale)
+    if not args.step_only:
+        result["host_block_manager"] = host_block_manager(wl2, wl4)
+        result["decode_graph"] = decode_graph_latency(pa, torch, b2, wl2, scale)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(b2, wl2)
     print(json.dumps(result), flush=True)
