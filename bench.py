@@ -76,6 +76,36 @@ def prefill_flops(wl, causal=True) -> int:
     return pairs * 4 * wl.head_dim * wl.num_q_heads
 
 
+def measured_peaks(torch, dev):
+    """Ceilings measured on this GPU after the timed steps (best of 10): a 1 GiB device-to-device copy
+    (read + written bytes) and a bf16 8192^3 matrix product through torch.matmul (the vendor GEMM),
+    reported beside the spec peaks. The prefill rooflines also give their fraction of the GEMM rate. The
+    copy is context only: it mixes reads and writes and runs below the decode kernel's pure read stream."""
+    def best_ms(fn, reps=10):
+        fn()
+        torch.cuda.synchronize()
+        best = float("inf")
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            best = min(best, a.elapsed_time(b))
+        return best
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    copy_gbs = 2 * src.numel() / (best_ms(lambda: dst.copy_(src)) * 1e-3) / 1e9
+    del src, dst
+    n = 8192
+    x = torch.randn((n, n), dtype=torch.bfloat16, device=dev)
+    y = torch.randn((n, n), dtype=torch.bfloat16, device=dev).contiguous()
+    gemm_tflops = 2 * n ** 3 / (best_ms(lambda: torch.matmul(x, y)) * 1e-3) / 1e12
+    del x, y
+    return {"copy_GBs": round(copy_gbs, 1), "bf16_gemm_TFLOPs": round(gemm_tflops, 1),
+            "note": "1 GiB device copy (read + write bytes); torch.matmul bf16 8192^3; best of 10"}
+
+
 def measured_traffic():
     """HBM bytes per pa_decode launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
     summary, or None if the decode kernel source or the compile flags changed since the
@@ -305,6 +335,12 @@ def main():
     wall = time.perf_counter() - t0
     ms = {name: float(np.mean([ev[i][n][0].elapsed_time(ev[i][n][1]) for i in range(args.steps)]))
           for n, name in enumerate(kernels)}
+    stats = {}
+    for n, name in enumerate(kernels):
+        t = [ev[i][n][0].elapsed_time(ev[i][n][1]) * 1e3 for i in range(args.steps)]
+        stats[name] = {"median": round(float(np.median(t)), 2), "min": round(float(np.min(t)), 2),
+                       "max": round(float(np.max(t)), 2)}
+    peaks = measured_peaks(torch, dev)
 
     dbytes = decode_bytes(wl2)
     decode_leg_ms = ms["store_decode"] + ms["decode"]
@@ -347,10 +383,12 @@ def main():
         "roofline_prefill": {"bound": "mfma", "kernel": "prefill_kernel (varlen, packed)", "achieved": round(t3, 1),
                              "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                              "frac": round(t3 / MFMA_BF16_PEAK_TFLOPS, 4),
+                             "frac_of_measured_gemm": round(t3 / peaks["bf16_gemm_TFLOPs"], 4),
                              "avg_launch_us": round(ms["prefill"] * 1e3, 2)},
         "roofline_prefix_prefill": {"bound": "mfma", "kernel": "prefill_kernel (block table)",
                                     "achieved": round(t4, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                                     "frac": round(t4 / MFMA_BF16_PEAK_TFLOPS, 4),
+                                    "frac_of_measured_gemm": round(t4 / peaks["bf16_gemm_TFLOPs"], 4),
                                     "avg_launch_us": round(ms["prefill_prefix"] * 1e3, 2)},
         "roofline_norm_rope_store": {"bound": "hbm", "kernel": "norm_rope_store_kernel (varlen prefill batch)",
                                      "achieved": round(nrb / (ms["norm_rope_prefill"] * 1e-3) / 1e9, 1),
@@ -364,6 +402,8 @@ def main():
                              "frac": round(smp_bytes / (ms["sample_decode"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                              "bytes_per_launch": smp_bytes, "avg_launch_us": round(ms["sample_decode"] * 1e3, 2)},
         "kernels_us": {k: round(v * 1e3, 2) for k, v in ms.items()},
+        "kernels_us_stats": stats,
+        "measured_peaks": peaks,
         "store_GBs": {k: round(sb[k] / (ms[k] * 1e-3) / 1e9, 1) for k in sb},
     }
     if args.copy_calibration:
