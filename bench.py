@@ -76,6 +76,46 @@ def prefill_flops(wl, causal=True) -> int:
     return pairs * 4 * wl.head_dim * wl.num_q_heads
 
 
+def long_decode(pa, torch, dev, steps=10, warmup=3):
+    """Store + decode of the long-context batch: 512 sequences, Hq 32 / Hkv 8 (G = 4), L log-uniform in
+    [256, 32768], a 164,794-block pool (60% of HBM for one layer's K and V)."""
+    from workloads import configs, tensors
+    wl5 = configs.config5()
+    b5 = tensors.materialize(wl5, dev, fill_nan=False)
+    scale = 1.0 / math.sqrt(wl5.head_dim)
+    ws = torch.empty(pa.pa_decode_workspace_size(wl5.num_seqs, 32, 8, 128, wl5.max_context_len),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty((wl5.num_seqs, 32, 128), dtype=torch.bfloat16, device=dev)
+    store = lambda: pa.pa_store_kvcache(b5.k_new, b5.v_new, b5.k_cache, b5.v_cache, b5.slot_mapping)  # noqa: E731
+    dec = lambda: pa.pa_decode(b5.q, b5.k_cache, b5.v_cache, b5.block_tables, b5.context_lens, scale,  # noqa: E731
+                               wl5.max_context_len, out=out, workspace=ws)
+    for _ in range(warmup):
+        store()
+        dec()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for e in ev:
+        e[0].record()
+        store()
+        e[1].record()
+        dec()
+        e[2].record()
+    torch.cuda.synchronize()
+    st = float(np.median([e[0].elapsed_time(e[1]) for e in ev]))
+    dt = float(np.median([e[1].elapsed_time(e[2]) for e in ev]))
+    db = decode_bytes(wl5)
+    res = {"workload": "decode step of 512 seqs, context log-uniform 256..32768 (Hq 32, Hkv 8, D 128, "
+                       "256-token blocks, 164,794-block pool)",
+           "kv_bytes": db["kv"], "store_us": round(st * 1e3, 2), "decode_us": round(dt * 1e3, 2),
+           "kv_GBs_step": round(db["kv"] / ((st + dt) * 1e-3) / 1e9, 1),
+           "decode_GBs": round(db["total"] / (dt * 1e-3) / 1e9, 1),
+           "frac": round(db["total"] / (dt * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "split_waves":
+               pa.pa_decode_split_waves(wl5.num_seqs, 32, 8, wl5.max_context_len)}
+    del b5, ws, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def measured_peaks(torch, dev):
     """Ceilings measured on this GPU after the timed steps (best of 10): a 1 GiB device-to-device copy
     (read + written bytes) and a bf16 8192^3 matrix product through torch.matmul (the vendor GEMM),
@@ -248,6 +288,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--split-waves", type=int, default=0, help="decode work split (0 = library choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--long-decode", action="store_true",
+                    help="also time store + decode of the long-context batch (512 seqs, Hq 32, L log-uniform "
+                         "256..32768, 164,794-block pool; about 14 GB of K/V per step), reported beside the line")
     ap.add_argument("--step-only", action="store_true",
                     help="skip the untimed host block-manager and decode-graph legs (profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -411,7 +454,9 @@ def main():
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
-    if not args.step_only:
+    if args.long_decode:
+        result["long_decode"] = long_decode(pa, torch, dev)
+    if not args.step_only and not args.long_decode:
         result["host_block_manager"] = host_block_manager(wl2, wl4)
         result["decode_graph"] = decode_graph_latency(pa, torch, b2, wl2, scale)
     if not args.no_cpu_baseline:
