@@ -79,6 +79,15 @@ struct ChunkRegs {
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// Lengths of sequences i0 .. i0 + 3, clamped to n - 1 so every load is valid:
+// the four loads are issued together and then pinned by an opaque use, so the
+// compiler can neither sink each into its own branch nor wait for each alone.
+__device__ __forceinline__ void load4_lens(const int32_t* lens, int i0, int n, int (&out)[4]) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u) out[u] = lens[min(i0 + u, n - 1)];
+  asm volatile("" : "+v"(out[0]), "+v"(out[1]), "+v"(out[2]), "+v"(out[3]));
+}
+
 struct Pos {
   int b, g, k;  // sequence, kv head, chunk within the pair (wave-uniform)
   int len, nc;  // context length and chunk count of sequence b
@@ -212,23 +221,6 @@ __device__ __forceinline__ int wave_inclusive_scan_i32(int x, int lane) {
 
 __device__ __forceinline__ int chunks_of(int len, int ch) { return len > 0 ? (len + ch - 1) / ch : 0; }
 
-// Chunks per kv head summed over sequences [0, upto) (wave-uniform result).
-// Each lane takes 4 consecutive sequences of a 256-sequence tile, so one
-// round of loads covers up to 256 sequences.
-__device__ __forceinline__ int64_t chunk_prefix(const int32_t* lens, int upto, int ch, int lane) {
-  int64_t run = 0;
-  for (int base = 0; base < upto; base += 256) {
-    int x = 0;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int b = base + lane * 4 + u;
-      x += b < upto ? chunks_of(lens[b], ch) : 0;
-    }
-    run += __builtin_amdgcn_readfirstlane(wave_sum_i32(x));
-  }
-  return run;
-}
-
 // First chunk index of wave w's share: floor(w * C / NW).
 __device__ __forceinline__ int64_t share_begin(int64_t w, int64_t total, int64_t nw) { return w * total / nw; }
 
@@ -332,7 +324,23 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(G >= 8 ? 1 :
   const int wave = blockIdx.x, lane = threadIdx.x;
   const int r = lane >> 3, s = lane & 7;
   const int64_t nw = a.num_waves;
-  const int64_t total = chunk_prefix(a.context_lens, a.num_seqs, CH, lane) * a.num_kv_heads;
+  // the first 256 lengths are loaded once and serve both scans below
+  int lu0[4];
+  load4_lens(a.context_lens, lane * 4, a.num_seqs, lu0);
+  int64_t total = 0;
+  for (int base = 0; base < a.num_seqs; base += 256) {
+    int x = 0, lu[4];
+    if (base == 0) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) lu[u] = lu0[u];
+    } else {
+      load4_lens(a.context_lens, base + lane * 4, a.num_seqs, lu);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) x += base + lane * 4 + u < a.num_seqs ? chunks_of(lu[u], CH) : 0;
+    total += uniform(wave_sum_i32(x));
+  }
+  total *= a.num_kv_heads;
   const int64_t lo = share_begin(wave, total, nw), hi = share_begin(wave + 1, total, nw);
   if (lo >= hi) return;
 
@@ -341,11 +349,17 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(G >= 8 ? 1 :
   {
     int64_t run = 0;
     for (int base = 0; base < a.num_seqs; base += 256) {
-      int len[4], x[4], sum = 0;
+      int len[4], x[4], sum = 0, lu[4];
+      if (base == 0) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) lu[u] = lu0[u];
+      } else {
+        load4_lens(a.context_lens, base + lane * 4, a.num_seqs, lu);
+      }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int b = base + lane * 4 + u;
-        len[u] = b < a.num_seqs ? a.context_lens[b] : 0;
+        len[u] = b < a.num_seqs ? lu[u] : 0;
         x[u] = chunks_of(len[u], CH) * a.num_kv_heads;
         sum += x[u];
       }
@@ -440,16 +454,33 @@ template <int G, int TPL>
 __global__ __launch_bounds__(64) void decode_finalize_kernel(DecodeArgs a) {
   constexpr int CH = 8 * TPL;
   const int b = blockIdx.x / a.num_kv_heads, g = blockIdx.x % a.num_kv_heads, lane = threadIdx.x;
-  const int len = a.context_lens[b];
-  const int nc = chunks_of(len, CH);
+  // One pass over the lengths (one round of loads): the chunks of sequence b,
+  // of the sequences before it, and of all sequences, per kv head.
+  int64_t before = 0, all = 0;
+  int nc = 0;
+  for (int base = 0; base < a.num_seqs; base += 256) {
+    int xb = 0, xa = 0, xm = 0, lu[4];
+    load4_lens(a.context_lens, base + lane * 4, a.num_seqs, lu);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int sq = base + lane * 4 + u;  // lanes past the end count 0
+      const int c = sq < a.num_seqs ? chunks_of(lu[u], CH) : 0;
+      xa += c;
+      xb += sq < b ? c : 0;
+      xm += sq == b ? c : 0;
+    }
+    all += uniform(wave_sum_i32(xa));
+    before += uniform(wave_sum_i32(xb));
+    nc += uniform(wave_sum_i32(xm));
+  }
   if (nc == 0) {
     uint32_t* o = reinterpret_cast<uint32_t*>(a.out + ((int64_t)b * a.num_q_heads + g * G) * kD);
     for (int i = lane; i < G * kD / 2; i += 64) o[i] = 0u;
     return;
   }
   const int64_t nw = a.num_waves;
-  const int64_t total = chunk_prefix(a.context_lens, a.num_seqs, CH, lane) * a.num_kv_heads;
-  const int64_t first = chunk_prefix(a.context_lens, b, CH, lane) * a.num_kv_heads + (int64_t)g * nc;
+  const int64_t total = all * a.num_kv_heads;
+  const int64_t first = before * a.num_kv_heads + (int64_t)g * nc;
   const int64_t w1 = wave_of_chunk(first, total, nw), w2 = wave_of_chunk(first + nc - 1, total, nw);
   if (w1 == w2) return;  // written whole by its wave
   float M[G], Ls[G], o0[G], o1[G];
@@ -465,31 +496,51 @@ __global__ __launch_bounds__(64) void decode_finalize_kernel(DecodeArgs a) {
     const bool live = w <= w2 && (w == w1 || share_begin(w, total, nw) < share_begin(w + 1, total, nw));
     const int64_t slot = w * 2 + (w == w1 ? 1 : 0);
     const int n = (int)min<int64_t>(64, w2 - wb + 1);
+    float2 ml[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+      ml[j] = live ? reinterpret_cast<const float2*>(a.ws_ml)[slot * G + j] : make_float2(kNegBig, 0.f);
+    float f[G];
 #pragma unroll
     for (int j = 0; j < G; ++j) {
-      const float2 ml = live ? reinterpret_cast<const float2*>(a.ws_ml)[slot * G + j] : make_float2(kNegBig, 0.f);
-      float mb = ml.x;
+      float mb = ml[j].x;
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) mb = fmaxf(mb, __shfl_xor(mb, off));
       const float mnew = fmaxf(M[j], mb);
       const float alpha = fast_exp2(M[j] - mnew);
-      const float f = live ? fast_exp2(ml.x - mnew) : 0.f;
-      float lf = f * ml.y;
+      f[j] = live ? fast_exp2(ml[j].x - mnew) : 0.f;
+      float lf = f[j] * ml[j].y;
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) lf += __shfl_xor(lf, off);
       Ls[j] = Ls[j] * alpha + lf;
       o0[j] *= alpha;
       o1[j] *= alpha;
       M[j] = mnew;
-      for (int i = 0; i < n; ++i) {
-        const float fi = __shfl(f, i);
+    }
+    // the pieces' rows, four pieces' loads in flight at a time, added in wave
+    // order (a piece with weight 0 is skipped; its slot may hold stale bits)
+    for (int i0 = 0; i0 < n; i0 += 4) {
+      float2 ov[4][G];
+      float fq[4][G];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i = min(i0 + q, n - 1);
         const int64_t si = __shfl(slot, i);
-        if (fi != 0.f) {
-          const float2 ov = reinterpret_cast<const float2*>(a.ws_o + (si * G + j) * kD)[lane];
-          o0[j] += fi * ov.x;
-          o1[j] += fi * ov.y;
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+          fq[q][j] = i0 + q < n ? __shfl(f[j], i) : 0.f;
+          ov[q][j] = reinterpret_cast<const float2*>(a.ws_o + (si * G + j) * kD)[lane];
         }
       }
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+          if (fq[q][j] != 0.f) {
+            o0[j] += fq[q][j] * ov[q][j].x;
+            o1[j] += fq[q][j] * ov[q][j].y;
+          }
+        }
     }
   }
 #pragma unroll
