@@ -2,7 +2,9 @@
 
 One step is one pass of the whole path over seeded synthetic batches:
   decode leg   store 256 new tokens + paged decode (256 seqs, L ~ U{100..2048},
-               Hq 16 / Hkv 8 / D 128, 256-token blocks, 4096-block pool);
+               Hq 16 / Hkv 8 / D 128, 256-token blocks, 4096-block pool), one
+               pa_store_decode launch (the separate pa_store_kvcache +
+               pa_decode calls are timed after the steps and reported beside);
   prefill leg  store + causal varlen prefill over packed q/k/v (about 29 seqs
                of 100..1024 tokens, at most 16384 tokens);
   prefix leg   store + prefix-cached prefill through the block table (32 seqs
@@ -11,9 +13,9 @@ One step is one pass of the whole path over seeded synthetic batches:
                q/k/v (one pass, reported as its own roofline);
   sampler leg  Gumbel-max sampling of one token for each of the 256 decode
                sequences over a 151936-token vocabulary (fp32 logits).
-After the timed steps (outside them): host timings of the C++ block manager,
-and the wall-clock decode-step latency eager vs graph-captured at batch 1, 16
-and 256.
+After the timed steps (outside them): the decode leg as two separate calls,
+host timings of the C++ block manager, and the wall-clock decode-step latency
+eager vs graph-captured at batch 1, 16 and 256.
 Inputs are resident in HBM before timing starts. `value` is the decode leg's
 KV-read throughput (bytes of K and V the decode must read, over the leg's
 time); the prefill legs report TFLOP/s of unmasked query-key pairs. Kernel
@@ -74,6 +76,33 @@ def prefill_flops(wl, causal=True) -> int:
     for a, b in zip(nq, nk):
         pairs += int((b - a) * a + a * (a + 1) // 2) if causal else int(a * b)
     return pairs * 4 * wl.head_dim * wl.num_q_heads
+
+
+def separate_decode_leg(pa, torch, b2, wl2, scale, mk2, ws, out2, args):
+    """The decode leg as pa_store_kvcache + pa_decode (two launches), median over the step count."""
+    def once(ev=None):
+        if ev is not None:
+            ev[0].record()
+        pa.pa_store_kvcache(b2.k_new, b2.v_new, b2.k_cache, b2.v_cache, b2.slot_mapping)
+        if ev is not None:
+            ev[1].record()
+        pa.pa_decode(b2.q, b2.k_cache, b2.v_cache, b2.block_tables, b2.context_lens, scale, mk2, out=out2,
+                     workspace=ws, split_waves=args.split_waves)
+        if ev is not None:
+            ev[2].record()
+    for _ in range(args.warmup):
+        once()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for e in evs:
+        once(e)
+    torch.cuda.synchronize()
+    st = float(np.median([e[0].elapsed_time(e[1]) for e in evs]))
+    dt = float(np.median([e[1].elapsed_time(e[2]) for e in evs]))
+    kv = decode_bytes(wl2)["kv"]
+    return {"store_us": round(st * 1e3, 2), "decode_us": round(dt * 1e3, 2),
+            "kv_GBs_leg": round(kv / ((st + dt) * 1e-3) / 1e9, 1),
+            "decode_GBs": round(decode_bytes(wl2)["total"] / (dt * 1e-3) / 1e9, 1)}
 
 
 def long_decode(pa, torch, dev, steps=10, warmup=3):
@@ -337,12 +366,12 @@ def main():
     smp_tokens = torch.empty(wl2.num_seqs, dtype=torch.int32, device=dev)
     smp_ws = torch.empty(pa.pa_sample_workspace_size(wl2.num_seqs, SAMPLER_VOCAB), dtype=torch.uint8, device=dev)
 
-    kernels = ["store_decode", "decode", "store_prefill", "prefill", "store_prefix", "prefill_prefix",
+    kernels = ["decode", "store_prefill", "prefill", "store_prefix", "prefill_prefix",
                "norm_rope_prefill", "sample_decode"]
     calls = {
-        "store_decode": lambda: pa.pa_store_kvcache(b2.k_new, b2.v_new, b2.k_cache, b2.v_cache, b2.slot_mapping),
-        "decode": lambda: pa.pa_decode(b2.q, b2.k_cache, b2.v_cache, b2.block_tables, b2.context_lens, scale, mk2,
-                                       out=out2, workspace=ws, split_waves=args.split_waves),
+        "decode": lambda: pa.pa_store_decode(b2.q, b2.k_new, b2.v_new, b2.k_cache, b2.v_cache, b2.block_tables,
+                                             b2.context_lens, scale, mk2, out=out2, workspace=ws,
+                                             split_waves=args.split_waves),
         "store_prefill": lambda: pa.pa_store_kvcache(b3.k_new, b3.v_new, b3.k_cache, b3.v_cache, b3.slot_mapping),
         "prefill": lambda: pa.pa_prefill_varlen(b3.q, b3.k_new, b3.v_new, b3.cu_seqlens_q, b3.cu_seqlens_k, mq3,
                                                 wl3.max_seqlen_k, scale, out=out3),
@@ -386,16 +415,15 @@ def main():
     peaks = measured_peaks(torch, dev)
 
     dbytes = decode_bytes(wl2)
-    decode_leg_ms = ms["store_decode"] + ms["decode"]
-    value = dbytes["kv"] / (decode_leg_ms * 1e-3) / 1e9
-    achieved = dbytes["total"] / (ms["decode"] * 1e-3) / 1e9
+    leg_bytes = dbytes["total"] + store_bytes(wl2, wl2.num_seqs)  # the decode plus the new tokens' store
+    value = dbytes["kv"] / (ms["decode"] * 1e-3) / 1e9
+    achieved = leg_bytes / (ms["decode"] * 1e-3) / 1e9
     f3, f4 = prefill_flops(wl3), prefill_flops(wl4)
     t3 = f3 / (ms["prefill"] * 1e-3) / 1e12
     t4 = f4 / (ms["prefill_prefix"] * 1e-3) / 1e12
     nrb = norm_rope_bytes(wl3, wl3.num_tokens)
     smp_bytes = wl2.num_seqs * (SAMPLER_VOCAB * 4 + 4 + 4)
-    sb = {"store_decode": store_bytes(wl2, wl2.num_seqs), "store_prefill": store_bytes(wl3, wl3.num_tokens),
-          "store_prefix": store_bytes(wl4, wl4.num_tokens)}
+    sb = {"store_prefill": store_bytes(wl3, wl3.num_tokens), "store_prefix": store_bytes(wl4, wl4.num_tokens)}
 
     result = {
         "metric": METRIC,
@@ -419,10 +447,10 @@ def main():
             "prefill_flops": f3,
             "prefix_prefill_flops": f4,
         },
-        "roofline": {"bound": "hbm", "kernel": "pa_decode (split + finalize kernels)",
+        "roofline": {"bound": "hbm", "kernel": "pa_store_decode (split kernel with the store fused + finalize)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
-                     "bytes_per_launch": dbytes["total"], "avg_launch_us": round(ms["decode"] * 1e3, 2)},
+                     "bytes_per_launch": leg_bytes, "avg_launch_us": round(ms["decode"] * 1e3, 2)},
         "roofline_prefill": {"bound": "mfma", "kernel": "prefill_kernel (varlen, packed)", "achieved": round(t3, 1),
                              "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                              "frac": round(t3 / MFMA_BF16_PEAK_TFLOPS, 4),
@@ -454,6 +482,8 @@ def main():
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
+    if not args.step_only:
+        result["decode_separate_calls"] = separate_decode_leg(pa, torch, b2, wl2, scale, mk2, ws, out2, args)
     if args.long_decode:
         result["long_decode"] = long_decode(pa, torch, dev)
     if not args.step_only and not args.long_decode:

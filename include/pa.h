@@ -188,6 +188,35 @@ int pa_decode(void* out, const void* q, int64_t q_seq_stride, const void* k_cach
               size_t workspace_bytes, void* stream);
 
 /*
+ * pa_store_decode — the decode step's store and pa_decode in one launch.
+ *
+ * Same result as pa_store_kvcache of each sequence's new token followed by
+ * pa_decode (page "nano-vLLM 最小化vLLM重新实现", section 5 "注意力机制": the
+ * new token's K/V are written to the paged cache, then decode attends over
+ * the cache): for every sequence b with L = context_lens[b] >= 1, row b of
+ * k_new / v_new (kv heads x dims) is written to position L - 1 of the
+ * sequence, i.e. row (L - 1) % block_size of block
+ * block_tables[b, (L - 1) / block_size], and out is pa_decode's output over
+ * positions 0 .. L - 1, the new token included. Sequences with L == 0 store
+ * nothing and give zero rows. The new token's position comes from the block
+ * table (no slot_mapping): the wave that reads the sequence's last chunk
+ * writes the row, waits for the write and then reads it, so no other work
+ * in the launch depends on it.
+ *
+ * k_new, v_new  [num_seqs, num_kv_heads, head_dim] bf16, heads x dims
+ *               contiguous, rows k_new_stride / v_new_stride elements apart
+ *               (16-byte aligned, at least num_kv_heads * head_dim).
+ * k_cache, v_cache  written (the new rows) and read.
+ * Every other argument, the workspace and the errors as in pa_decode.
+ */
+int pa_store_decode(void* out, const void* q, int64_t q_seq_stride, const void* k_new, int64_t k_new_stride,
+                    const void* v_new, int64_t v_new_stride, void* k_cache, void* v_cache,
+                    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                    int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t block_size, int32_t max_context_len, float scale, int32_t split_waves, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/*
  * pa_prefill_varlen — attention over packed variable-length sequences.
  *
  * Page "nano-vLLM 最小化vLLM重新实现", section 5 "注意力机制": prefill over

@@ -16,8 +16,8 @@ from . import _lib
 from ._lib import LibraryMissing  # noqa: F401
 
 __all__ = [
-    "PAError", "LibraryMissing", "pa_store_kvcache", "pa_qk_norm_rope_store", "pa_decode", "pa_decode_workspace_size",
-    "pa_decode_split_waves", "pa_prefill_varlen", "pa_status_string", "pa_last_error", "pa_version",
+    "PAError", "LibraryMissing", "pa_store_kvcache", "pa_qk_norm_rope_store", "pa_decode", "pa_store_decode",
+    "pa_decode_workspace_size", "pa_decode_split_waves", "pa_prefill_varlen", "pa_status_string", "pa_last_error", "pa_version",
     "library_path", "DecodeGraphs", "pa_sample_gumbel", "pa_sample_workspace_size",
 ]
 
@@ -152,6 +152,30 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, max
         _ptr(out), _ptr(q), _rows(q, "q"), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
         int(block_tables.shape[1]), _ptr(context_lens), b, hq, hkv, d, bs, int(max_context_len), float(scale),
         int(split_waves), _ptr(workspace), ws_bytes, _stream(stream, q.device)))
+    return out
+
+
+def pa_store_decode(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale: float,
+                    max_context_len: int, out=None, workspace=None, split_waves: int = 0, stream=None):
+    """Store each sequence's new token at position L - 1 (through its block table), then paged decode:
+    q [B, Hq, D], k_new / v_new [B, Hkv, D] bf16 -> out [B, Hq, D] bf16, in one launch.
+
+    workspace: as for pa_decode (allocated here when not given).
+    """
+    lib = _lib.load()
+    b, hq, d = q.shape
+    nb, bs, hkv, _ = k_cache.shape
+    if out is None:
+        out = torch.empty((b, hq, d), dtype=torch.bfloat16, device=q.device)
+    need = lib.pa_decode_workspace_size(b, hq, hkv, d, max_context_len, split_waves)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("pa_store_decode", lib.pa_store_decode(
+        _ptr(out), _ptr(q), _rows(q, "q"), _ptr(k_new), _rows(k_new, "k_new"), _ptr(v_new), _rows(v_new, "v_new"),
+        _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), int(block_tables.shape[1]), _ptr(context_lens), b, hq,
+        hkv, d, bs, int(max_context_len), float(scale), int(split_waves), _ptr(workspace), ws_bytes,
+        _stream(stream, q.device)))
     return out
 
 

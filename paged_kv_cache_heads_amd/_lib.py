@@ -34,6 +34,8 @@ SIGNATURES = {
     "pa_decode_split_waves": (_i32, [_i32, _i32, _i32, _i32, _i32]),
     "pa_decode": (ctypes.c_int, [_vp, _vp, _i64, _vp, _vp, _i32p, _i32, _i32p, _i32, _i32, _i32, _i32, _i32, _i32,
                                  _f32, _i32, _vp, _sz, _vp]),
+    "pa_store_decode": (ctypes.c_int, [_vp, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _i32p, _i32, _i32p, _i32,
+                                       _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp]),
     "pa_prefill_varlen": (ctypes.c_int, [_vp, _vp, _i64, _vp, _vp, _i64, _i64, _i32p, _i32p, _i32, _i32, _i32, _i32,
                                          _i32, _i32, _f32, _i32, _i32p, _i32, _i32, _vp]),
     "pa_sample_workspace_size": (_sz, [_i32, _i32]),

@@ -109,7 +109,30 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<TPL>& c, const DecodeArgs& 
   const char* kb = reinterpret_cast<const char*>(a.k_cache + base);
   const char* vb = reinterpret_cast<const char*>(a.v_cache + base);
   const int nvalid = p.len - tok0;
-  if (nvalid >= CH) {
+  if (a.k_new && p.k == p.nc - 1) {
+    // Fused store (pa_store_decode): the sequence's new token, position L - 1,
+    // is read from k_new / v_new row b (kv head g) instead of the cache, which
+    // the finalize pass writes it to once this kernel is done. This chunk is
+    // the only reader of that position, so no work waits on the store.
+    const char* kn = reinterpret_cast<const char*>(a.k_new + p.b * a.k_new_stride + p.g * kD) + 16 * s;
+    const char* vn = reinterpret_cast<const char*>(a.v_new + p.b * a.v_new_stride + p.g * kD) + 16 * s;
+#pragma unroll
+    for (int i = 0; i < TPL; ++i) {
+      const int tok = min(i * 8 + r, nvalid - 1);
+      const uint32_t off = (uint32_t)tok * row_bytes + 16 * s;
+      const char* kp = tok == nvalid - 1 ? kn : kb + off;
+      c.k[i][0] = load16_nt(kp);
+      c.k[i][1] = load16_nt(kp + 128);
+    }
+#pragma unroll
+    for (int i = 0; i < TPL; ++i) {
+      const int tok = min(i * 8 + r, nvalid - 1);
+      const uint32_t off = (uint32_t)tok * row_bytes + 16 * s;
+      const char* vp = tok == nvalid - 1 ? vn : vb + off;
+      c.v[i][0] = load16_nt(vp);
+      c.v[i][1] = load16_nt(vp + 128);
+    }
+  } else if (nvalid >= CH) {
 #pragma unroll
     for (int i = 0; i < TPL; ++i) {
       const uint32_t off = lane_off + i * 8 * row_bytes;
@@ -477,6 +500,20 @@ __global__ __launch_bounds__(64) void decode_finalize_kernel(DecodeArgs a) {
     uint32_t* o = reinterpret_cast<uint32_t*>(a.out + ((int64_t)b * a.num_q_heads + g * G) * kD);
     for (int i = lane; i < G * kD / 2; i += 64) o[i] = 0u;
     return;
+  }
+  if (a.k_new && lane < 32) {
+    // fused store (pa_store_decode): the new token's K and V rows of kv head g go
+    // to position L - 1 (the split kernel read them from k_new / v_new); lanes
+    // 0-15 move 16 B of the K row each, lanes 16-31 of the V row
+    const int len = a.context_lens[b];
+    const int pos = len - 1;
+    const int blk = a.block_tables[(int64_t)b * a.max_blocks_per_seq + pos / a.block_size];
+    const int64_t row = ((int64_t)blk * a.block_size + pos % a.block_size) * a.num_kv_heads * kD + g * kD;
+    const bool is_v = lane >= 16;
+    const int d = (lane & 15) * 8;
+    const uint16_t* src = (is_v ? a.v_new + b * a.v_new_stride : a.k_new + b * a.k_new_stride) + g * kD + d;
+    uint16_t* dst = const_cast<uint16_t*>(is_v ? a.v_cache : a.k_cache) + row + d;
+    *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
   }
   const int64_t nw = a.num_waves;
   const int64_t total = all * a.num_kv_heads;

@@ -32,6 +32,10 @@ struct DecodeArgs {
   const uint16_t* v_cache;
   const int32_t* block_tables;
   const int32_t* context_lens;
+  const uint16_t* k_new;  // fused store (pa_store_decode): the new token's K row per sequence, else null
+  const uint16_t* v_new;
+  int64_t k_new_stride;   // elements between sequences' rows
+  int64_t v_new_stride;
   float* ws_o;   // [num_waves * 2 slots, G, head_dim] partial outputs
   float* ws_ml;  // [num_waves * 2 slots, G, 2] (max, sum) of each partial
   int32_t max_blocks_per_seq;

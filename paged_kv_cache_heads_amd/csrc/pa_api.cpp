@@ -266,11 +266,14 @@ int32_t pa_decode_split_waves(int32_t num_seqs, int32_t num_q_heads, int32_t num
   return g.num_waves;
 }
 
-int pa_decode(void* out, const void* q, int64_t q_seq_stride, const void* k_cache, const void* v_cache,
-              const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
-              int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-              int32_t max_context_len, float scale, int32_t split_waves, void* workspace,
-              size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+static int decode_impl(void* out, const void* q, int64_t q_seq_stride, const void* k_new, int64_t k_new_stride,
+                       const void* v_new, int64_t v_new_stride, const void* k_cache, const void* v_cache,
+                       const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                       int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t block_size, int32_t max_context_len, float scale, int32_t split_waves, void* workspace,
+                       size_t workspace_bytes, void* stream) {
   if (num_seqs < 0) return fail(PA_ERR_INVALID_ARGUMENT, "num_seqs %d is negative", num_seqs);
   if (num_seqs > 65535) return fail(PA_ERR_UNSUPPORTED, "num_seqs %d exceeds 65535", num_seqs);
   int st = check_heads(num_q_heads, num_kv_heads, head_dim);
@@ -293,6 +296,14 @@ int pa_decode(void* out, const void* q, int64_t q_seq_stride, const void* k_cach
                 (long long)q_seq_stride);
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || q_seq_stride % 8)
     return fail(PA_ERR_ALIGNMENT, "out, q, caches and q_seq_stride must be 16-byte aligned");
+  if (k_new || v_new) {
+    if (!k_new || !v_new) return fail(PA_ERR_NULL_POINTER, "k_new and v_new are required");
+    if (k_new_stride < (int64_t)num_kv_heads * head_dim || v_new_stride < (int64_t)num_kv_heads * head_dim)
+      return fail(PA_ERR_INVALID_ARGUMENT, "k_new / v_new strides (%lld, %lld) are below num_kv_heads * head_dim",
+                  (long long)k_new_stride, (long long)v_new_stride);
+    if (!aligned16(k_new) || !aligned16(v_new) || k_new_stride % 8 || v_new_stride % 8)
+      return fail(PA_ERR_ALIGNMENT, "k_new, v_new and their strides must be 16-byte aligned");
+  }
   DecodeGeometry g;
   decode_geometry(num_seqs, num_q_heads, num_kv_heads, max_context_len, split_waves, &g);
   if (!workspace) return fail(PA_ERR_NULL_POINTER, "workspace of %zu bytes is required", g.ws_bytes);
@@ -307,6 +318,10 @@ int pa_decode(void* out, const void* q, int64_t q_seq_stride, const void* k_cach
   a.v_cache = static_cast<const uint16_t*>(v_cache);
   a.block_tables = block_tables;
   a.context_lens = context_lens;
+  a.k_new = static_cast<const uint16_t*>(k_new);
+  a.v_new = static_cast<const uint16_t*>(v_new);
+  a.k_new_stride = k_new_stride;
+  a.v_new_stride = v_new_stride;
   a.ws_o = static_cast<float*>(workspace);
   a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + g.ws_o_bytes);
   a.max_blocks_per_seq = max_blocks_per_seq;
@@ -318,6 +333,30 @@ int pa_decode(void* out, const void* q, int64_t q_seq_stride, const void* k_cach
   a.scale_log2e = scale * kLog2e;
   return hip_status(pa::launch_decode(a, num_q_heads / num_kv_heads, static_cast<hipStream_t>(stream)),
                     "decode launch");
+}
+
+extern "C" {
+
+int pa_decode(void* out, const void* q, int64_t q_seq_stride, const void* k_cache, const void* v_cache,
+              const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+              int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+              int32_t max_context_len, float scale, int32_t split_waves, void* workspace,
+              size_t workspace_bytes, void* stream) {
+  return decode_impl(out, q, q_seq_stride, nullptr, 0, nullptr, 0, k_cache, v_cache, block_tables,
+                     max_blocks_per_seq, context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                     max_context_len, scale, split_waves, workspace, workspace_bytes, stream);
+}
+
+int pa_store_decode(void* out, const void* q, int64_t q_seq_stride, const void* k_new, int64_t k_new_stride,
+                    const void* v_new, int64_t v_new_stride, void* k_cache, void* v_cache,
+                    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                    int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t block_size, int32_t max_context_len, float scale, int32_t split_waves, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  if (num_seqs > 0 && (!k_new || !v_new)) return fail(PA_ERR_NULL_POINTER, "k_new and v_new are required");
+  return decode_impl(out, q, q_seq_stride, k_new, k_new_stride, v_new, v_new_stride, k_cache, v_cache, block_tables,
+                     max_blocks_per_seq, context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                     max_context_len, scale, split_waves, workspace, workspace_bytes, stream);
 }
 
 int pa_prefill_varlen(void* out, const void* q, int64_t q_token_stride, const void* k, const void* v,

@@ -112,6 +112,26 @@ def test_decode_validation(lib):
     assert decode(lib, B=0, out=None, q=None, kc=None, vc=None, bt=None, cl=None) == PA_OK
 
 
+def store_decode(lib, **kw):
+    a = dict(out=A, q=A, qs=2048, kn=A, kns=1024, vn=A, vns=1024, kc=A, vc=A, bt=A, W=8, cl=A, B=4, hq=16, hkv=8,
+             d=128, bs=256, maxL=2048, scale=0.088, part=0, ws=A, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return lib.pa_store_decode(a["out"], a["q"], a["qs"], a["kn"], a["kns"], a["vn"], a["vns"], a["kc"], a["vc"],
+                               a["bt"], a["W"], a["cl"], a["B"], a["hq"], a["hkv"], a["d"], a["bs"], a["maxL"],
+                               a["scale"], a["part"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_store_decode_validation(lib):
+    assert store_decode(lib, kn=None) == NULLP
+    assert store_decode(lib, vn=None) == NULLP
+    assert store_decode(lib, kns=512) == INVAL          # below num_kv_heads * head_dim
+    assert store_decode(lib, vns=1028) == ALIGN          # not a multiple of 8 elements
+    assert store_decode(lib, kn=A + 2) == ALIGN
+    assert store_decode(lib, W=7) == INVAL               # the decode checks apply too
+    assert store_decode(lib, ws=None) == NULLP
+    assert store_decode(lib, B=0, out=None, q=None, kn=None, vn=None, kc=None, vc=None, bt=None, cl=None) == PA_OK
+
+
 def test_decode_workspace_size(lib):
     # G = 2: 32-token chunks; 256 seqs x 8 kv heads x 64 chunks leave the default 2048 waves
     assert lib.pa_decode_split_waves(256, 16, 8, 2048, 0) == 2048
