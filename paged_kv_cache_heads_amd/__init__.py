@@ -43,6 +43,35 @@ def _ptr(t) -> int:
     return 0 if t is None else t.data_ptr()
 
 
+_BF16, _I32, _F32, _U8 = torch.bfloat16, torch.int32, torch.float32, torch.uint8
+
+
+def _want(t, name: str, dtype, dim=None, contiguous=False, device=None, optional=False):
+    """Check a tensor argument before its address crosses the C ABI (which sees only pointers).
+
+    Raises TypeError for a non-tensor or a wrong dtype and ValueError for a wrong rank, a required
+    but missing contiguity, a tensor off the GPU or on another device than the call's. Returns
+    the tensor's device.
+    """
+    if t is None:
+        if optional:
+            return device
+        raise TypeError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if dim is not None and t.dim() != dim:
+        raise ValueError(f"{name} must have {dim} dimensions, got shape {tuple(t.shape)}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU, got {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, other arguments on {device}")
+    return t.device
+
+
 def _stream(stream, device) -> int:
     if stream is not None:
         return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
@@ -71,6 +100,11 @@ def pa_version() -> int:
 
 def pa_store_kvcache(k, v, k_cache, v_cache, slot_mapping, stream=None) -> None:
     """Write k[t] / v[t] ([T, Hkv, D] bf16) into the caches ([NB, bs, Hkv, D]) at slot_mapping[t]."""
+    dev = _want(k_cache, "k_cache", _BF16, 4, True)
+    _want(v_cache, "v_cache", _BF16, 4, True, dev)
+    _want(k, "k", _BF16, 3, device=dev)
+    _want(v, "v", _BF16, 3, device=dev)
+    _want(slot_mapping, "slot_mapping", _I32, 1, True, dev)
     lib = _lib.load()
     nb, bs, hkv, d = k_cache.shape
     _check("pa_store_kvcache", lib.pa_store_kvcache(
@@ -85,6 +119,15 @@ def pa_qk_norm_rope_store(qkv, q_norm_weight, k_norm_weight, eps: float, cos_sin
     cos_sin: [max_position, D] fp32 (cosines, then sines); positions, slot_mapping: [T] int32.
     Returns q_out [T, Hq, D] bf16 (allocated when not given; may be a view of qkv's q columns).
     """
+    dev = _want(qkv, "qkv", _BF16, 2)
+    for name, x in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _want(x, name, _BF16, 4, True, dev)
+    for name, x in (("q_norm_weight", q_norm_weight), ("k_norm_weight", k_norm_weight)):
+        _want(x, name, _BF16, 1, True, dev)
+    _want(cos_sin, "cos_sin", _F32, 2, True, dev)
+    _want(positions, "positions", _I32, 1, True, dev)
+    _want(slot_mapping, "slot_mapping", _I32, 1, True, dev)
+    _want(q_out, "q_out", _BF16, 3, device=dev, optional=True)
     lib = _lib.load()
     nb, bs, hkv, d = k_cache.shape
     t = int(qkv.shape[0])
@@ -105,6 +148,10 @@ def pa_sample_workspace_size(num_rows: int, vocab_size: int) -> int:
 
 def pa_sample_gumbel(logits, temperatures, seed: int, offset: int, tokens=None, workspace=None, stream=None):
     """One token per row of logits [B, V] fp32 (temperatures [B] fp32): int32 [B]."""
+    dev = _want(logits, "logits", _F32, 2)
+    _want(temperatures, "temperatures", _F32, 1, True, dev)
+    _want(tokens, "tokens", _I32, 1, True, dev, optional=True)
+    _want(workspace, "workspace", _U8, 1, True, dev, optional=True)
     lib = _lib.load()
     b, v = int(logits.shape[0]), int(logits.shape[1])
     if logits.dim() != 2 or logits.stride(1) != 1:
@@ -132,6 +179,17 @@ def pa_decode_split_waves(num_seqs, num_q_heads, num_kv_heads, max_context_len, 
                                                  split_waves))
 
 
+def _decode_args(q, k_cache, v_cache, block_tables, context_lens, out, workspace):
+    dev = _want(q, "q", _BF16, 3)
+    _want(k_cache, "k_cache", _BF16, 4, True, dev)
+    _want(v_cache, "v_cache", _BF16, 4, True, dev)
+    _want(block_tables, "block_tables", _I32, 2, True, dev)
+    _want(context_lens, "context_lens", _I32, 1, True, dev)
+    _want(out, "out", _BF16, 3, True, dev, optional=True)
+    _want(workspace, "workspace", _U8, 1, True, dev, optional=True)
+    return dev
+
+
 def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, max_context_len: int, out=None,
               workspace=None, split_waves: int = 0, stream=None):
     """Paged decode: q [B, Hq, D] bf16 -> out [B, Hq, D] bf16.
@@ -139,6 +197,7 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, max
     workspace: a uint8 device tensor of at least pa_decode_workspace_size(...)
     bytes; allocated here when not given.
     """
+    _decode_args(q, k_cache, v_cache, block_tables, context_lens, out, workspace)
     lib = _lib.load()
     b, hq, d = q.shape
     nb, bs, hkv, _ = k_cache.shape
@@ -162,6 +221,9 @@ def pa_store_decode(q, k_new, v_new, k_cache, v_cache, block_tables, context_len
 
     workspace: as for pa_decode (allocated here when not given).
     """
+    dev = _decode_args(q, k_cache, v_cache, block_tables, context_lens, out, workspace)
+    _want(k_new, "k_new", _BF16, 3, device=dev)
+    _want(v_new, "v_new", _BF16, 3, device=dev)
     lib = _lib.load()
     b, hq, d = q.shape
     nb, bs, hkv, _ = k_cache.shape
@@ -186,6 +248,14 @@ def pa_prefill_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, ma
     Without block_table, k / v are packed [Tk, Hkv, D] (row strides may exceed
     Hkv * D); with it, k / v are the caches [NB, bs, Hkv, D].
     """
+    dev = _want(q, "q", _BF16, 3)
+    kdim = 3 if block_table is None else 4
+    _want(k, "k", _BF16, kdim, block_table is not None, dev)
+    _want(v, "v", _BF16, kdim, block_table is not None, dev)
+    _want(cu_seqlens_q, "cu_seqlens_q", _I32, 1, True, dev)
+    _want(cu_seqlens_k, "cu_seqlens_k", _I32, 1, True, dev)
+    _want(block_table, "block_table", _I32, 2, True, dev, optional=True)
+    _want(out, "out", _BF16, 3, True, dev, optional=True)
     lib = _lib.load()
     tq, hq, d = q.shape
     if out is None:
@@ -218,6 +288,11 @@ class DecodeGraphs:
                  v_cache, scale: float, max_context_len: int, batch_sizes, split_waves: int = 0, stream=None):
         import ctypes
 
+        dev = _decode_args(q, k_cache, v_cache, block_tables, context_lens, out, workspace)
+        _want(workspace, "workspace", _U8, 1, True, dev)
+        _want(k_new, "k_new", _BF16, 3, device=dev)
+        _want(v_new, "v_new", _BF16, 3, device=dev)
+        _want(slot_mapping, "slot_mapping", _I32, 1, True, dev)
         lib = _lib.load()
         self._lib = lib
         nb, bs, hkv, d = k_cache.shape
