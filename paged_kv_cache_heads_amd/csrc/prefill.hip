@@ -190,15 +190,31 @@ void prefill_kernel(PrefillArgs a) {
   constexpr int PB = QP / 16;  // 16-position subtiles per head
   // Work item of this workgroup. Workgroup ids are dealt to the 8 XCDs
   // round-robin (id % 8) and each XCD has its own L2, so XCD x takes the
-  // contiguous slice x of the items ordered by (kv head, sequence, query tile
-  // from the last): the workgroups running together on one XCD then share
-  // the K/V of a few sequences, which stays in that L2 across their query
-  // tiles, instead of streaming a different sequence's K/V per workgroup.
+  // contiguous slice x of the items, ordered kv head first. Under the causal
+  // mask a query tile costs in proportion to its index, so within a head the
+  // items go heaviest first: the query tiles are taken in pairs from the
+  // last one down (tiles T-1 and T-2 of every sequence, then T-3 and T-4 of
+  // every sequence, ...; with T odd, tile 0 alone at the end), sequence by
+  // sequence within a pair. The long tiles then start in the first wave of
+  // workgroups and the short ones fill the tail, while the two tiles of a
+  // pair still read the same sequence's K/V through the XCD's L2.
   const int64_t item = (int64_t)(blockIdx.x & 7) * a.items_per_xcd + (blockIdx.x >> 3);
-  if (item >= (int64_t)a.num_kv_heads * a.num_seqs * a.num_q_tiles) return;
-  const int qtile = a.num_q_tiles - 1 - (int)(item % a.num_q_tiles);
-  const int seq = (int)((item / a.num_q_tiles) % a.num_seqs);
-  const int kvh = (int)(item / ((int64_t)a.num_q_tiles * a.num_seqs));
+  const int64_t per_head = (int64_t)a.num_q_tiles * a.num_seqs;
+  if (item >= (int64_t)a.num_kv_heads * per_head) return;
+  const int kvh = (int)(item / per_head);
+  const int64_t r = item - (int64_t)kvh * per_head;
+  const int64_t pair_items = 2 * (int64_t)a.num_seqs;
+  const int64_t paired = pair_items * (a.num_q_tiles / 2);
+  int seq, qtile;
+  if (r < paired) {
+    const int pair = (int)(r / pair_items);
+    const int w = (int)(r - pair * pair_items);
+    seq = w >> 1;
+    qtile = a.num_q_tiles - 1 - 2 * pair - (w & 1);
+  } else {
+    seq = (int)(r - paired);
+    qtile = 0;
+  }
   const int q_beg = a.cu_seqlens_q[seq];
   const int nq = a.cu_seqlens_q[seq + 1] - q_beg;
   const int k_beg = a.cu_seqlens_k[seq];
