@@ -476,6 +476,12 @@ def main():
         "kernels_us_stats": stats,
         "measured_peaks": peaks,
         "store_GBs": {k: round(sb[k] / (ms[k] * 1e-3) / 1e9, 1) for k in sb},
+        "roofline_store": {k: {"bound": "hbm", "kernel": "store_tokens_kernel (%s batch)" % (
+                                   "varlen" if k == "store_prefill" else "prefix"),
+                               "achieved": round(sb[k] / (ms[k] * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                               "unit": "GB/s", "frac": round(sb[k] / (ms[k] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                               "frac_of_measured_copy": round(sb[k] / (ms[k] * 1e-3) / 1e9 / peaks["copy_GBs"], 4),
+                               "bytes_per_launch": sb[k], "avg_launch_us": round(ms[k] * 1e3, 2)} for k in sb},
     }
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)

@@ -83,3 +83,30 @@ def test_store_empty(dev):
     pa.pa_store_kvcache(e, e, kc, kc, torch.zeros(0, dtype=torch.int32, device=dev))
     torch.cuda.synchronize()
     assert int(kc.abs().sum()) == 0
+
+
+@pytest.mark.parametrize("hkv,head_dim,tokens", [(1, 128, 37), (2, 64, 5), (3, 128, 29), (4, 128, 258), (8, 128, 1),
+                                                 (8, 128, 513), (16, 128, 33), (6, 64, 17), (1, 8, 300)])
+def test_store_head_layouts(dev, hkv, head_dim, tokens):
+    """Both layouts of the store kernel: whole tokens per workgroup (K+V row a
+    power of two of 16-byte vectors up to 256: hkv 1/2/4/8 at 128 dims, the
+    8-element row) and the flat one (hkv 3, 6, 16); odd token counts, strided
+    sources, padded slots."""
+    announce(f"store hkv {hkv} head_dim {head_dim} tokens {tokens}")
+    rng = np.random.default_rng([hkv, head_dim, tokens])
+    nb, bs = 24, 32
+    row = hkv * head_dim
+    src = torch.from_numpy(rng.integers(0, 1 << 16, size=(tokens, 3 * row), dtype=np.uint16).view(np.int16)).to(dev)
+    k = src[:, row:2 * row].view(torch.bfloat16).unflatten(1, (hkv, head_dim))
+    v = src[:, 2 * row:].view(torch.bfloat16).unflatten(1, (hkv, head_dim))
+    slots_np = rng.permutation(nb * bs)[:tokens].astype(np.int32)
+    slots_np[rng.random(tokens) < 0.1] = -1
+    slots = torch.from_numpy(slots_np).to(dev)
+    kc = torch.full((nb, bs, hkv, head_dim), -1, dtype=torch.int16, device=dev).view(torch.bfloat16)
+    vc = torch.full((nb, bs, hkv, head_dim), -2, dtype=torch.int16, device=dev).view(torch.bfloat16)
+    kc0, vc0 = tensors.to_u16(kc), tensors.to_u16(vc)
+    pa.pa_store_kvcache(k, v, kc, vc, slots)
+    torch.cuda.synchronize()
+    kref, vref = oracle.store_kvcache(tensors.to_u16(k), tensors.to_u16(v), slots_np, kc0, vc0)
+    assert np.array_equal(tensors.to_u16(kc), kref)
+    assert np.array_equal(tensors.to_u16(vc), vref)
