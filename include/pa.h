@@ -269,9 +269,9 @@ int pa_prefill_varlen(void* out, const void* q, int64_t q_token_stride, const vo
  *   tokens[b] = argmax_i softmax(l / T)_i / E_i,  E_i = -ln(u_i),
  * which draws token i with probability softmax(l / T)_i. u_i comes from
  * Philox4x64-10 (Salmon et al., SC 2011) under key (seed, 0): element i takes
- * a 23-bit field w of 64-bit word (i / 2) % 4 of the block at counter
- * (i / 8, b, offset, 0) -- bits 63..41 for even i, 40..18 for odd i -- and
- * u = (w + 1/2) / 2^23. Pass a new offset (e.g. the step number) for new
+ * a 21-bit field w of 64-bit word (i / 3) % 4 of the block at counter
+ * (i / 12, b, offset, 0) -- bits 63..43, 42..22 or 21..1 for i % 3 = 0, 1,
+ * 2 -- and u = (w + 1/2) / 2^21. Pass a new offset (e.g. the step number) for new
  * noise. The decision is taken in fp32 (l log2(e) / T - log2(-log2(u))); ties
  * go to the lowest index; -inf logits are never drawn unless a whole row is
  * -inf (then token 0 by the tie rule); NaN logits give an unspecified token in

@@ -32,17 +32,17 @@ def check_philox_matches_numpy(orc, seed=0):
 
 
 def check_uniforms_from_numpy_words(orc):
-    # element i of row b: 23-bit field of word (i // 2) % 4 of the block at counter
-    # (i // 8, b, offset, 0), key (seed, 0): bits 63..41 (even i) or 40..18 (odd i);
-    # u = (field + 1/2) / 2^23. Blocks j >= 1 are compared (numpy cannot start below counter 0).
-    seed, offset, rows, vocab = 123456789, 7, 3, 45
+    # element i of row b: 21-bit field of word (i // 3) % 4 of the block at counter
+    # (i // 12, b, offset, 0), key (seed, 0): bits 63..43, 42..22 or 21..1 for i % 3 = 0, 1, 2;
+    # u = (field + 1/2) / 2^21. Blocks j >= 1 are compared (numpy cannot start below counter 0).
+    seed, offset, rows, vocab = 123456789, 7, 3, 61
     u = orc.uniforms(rows, vocab, seed, offset)
     assert u.shape == (rows, vocab)
     for b in range(rows):
-        for i in range(8, vocab):
-            w = int(_numpy_block([i // 8, b, offset, 0], [seed, 0])[(i // 2) % 4])
-            field = (w >> 41) if i % 2 == 0 else (w >> 18) & 0x7FFFFF
-            assert u[b, i] == (field + 0.5) / 2.0 ** 23, (b, i)
+        for i in range(12, vocab):
+            w = int(_numpy_block([i // 12, b, offset, 0], [seed, 0])[(i // 3) % 4])
+            field = (w >> (43 - 21 * (i % 3))) % (1 << 21)
+            assert u[b, i] == (field + 0.5) / 2.0 ** 21, (b, i)
     assert np.all(u > 0) and np.all(u < 1)
     assert np.array_equal(u.astype(np.float32).astype(np.float64), u)  # exact in fp32
 

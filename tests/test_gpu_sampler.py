@@ -44,7 +44,7 @@ def _check(got, logits, temps, seed, offset):
     return int((~separated).sum())
 
 
-@pytest.mark.parametrize("vocab", [1, 7, 8, 9, 8191, 8192, 8193, 20000])
+@pytest.mark.parametrize("vocab", [1, 7, 8, 9, 11, 12, 13, 8191, 8192, 8193, 12287, 12288, 12289, 20000])
 def test_sampler_small(dev, vocab):
     announce(f"sampler vocab {vocab}")
     rng = np.random.default_rng(vocab)

@@ -15,9 +15,11 @@ MUTANTS = {
     "philox_lo_hi_swapped": ("x = [hi1 ^ x[1] ^ k0, lo1, hi0 ^ x[3] ^ k1, lo0]",
                              "x = [lo1 ^ x[1] ^ k0, hi1, lo0 ^ x[3] ^ k1, hi0]"),
     "key_not_bumped": ("            k1 = k1 + W1\n", "            k1 = k1\n"),
-    "uniform_low_bits": ("fields[:, 0::2] = words >> np.uint64(41)", "fields[:, 0::2] = words & np.uint64(0x7FFFFF)"),
-    "fields_swapped": ("fields[:, 0::2] = words >> np.uint64(41)\n    fields[:, 1::2] = (words >> np.uint64(18))",
-                       "fields[:, 1::2] = words >> np.uint64(41)\n    fields[:, 0::2] = (words >> np.uint64(18))"),
+    "uniform_low_bits": ("fields[:, 0::3] = words >> np.uint64(43)", "fields[:, 0::3] = words & mask"),
+    "fields_swapped": ("fields[:, 0::3] = words >> np.uint64(43)\n    fields[:, 1::3] = (words >> np.uint64(22))",
+                       "fields[:, 1::3] = words >> np.uint64(43)\n    fields[:, 0::3] = (words >> np.uint64(22))"),
+    "third_field_unshifted": ("fields[:, 2::3] = (words >> np.uint64(1)) & mask", "fields[:, 2::3] = words & mask"),
+    "two_to_the_23": ("/ 2.0 ** 21", "/ 2.0 ** 23"),
     "counter_row_and_block_swapped": ("ctr = np.stack([j, b,", "ctr = np.stack([b, j,"),
     "noise_is_uniform": ("e = -np.log(u)", "e = u"),
     "multiplies_by_noise": ("- np.log(e)", "+ np.log(e)"),
