@@ -137,6 +137,25 @@ __device__ __forceinline__ void wait_lds_le(v2i_t& x, v2i_t& y) {
   asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(x), "+v"(y) : "i"(N));
 }
 
+typedef int v4i_t __attribute__((ext_vector_type(4)));
+
+// ds_read_b128 at addr + OFF, issued as inline assembly for the same reason
+// as the transposed reads: its result is used only after wait_lds_le1 has
+// covered it.
+template <int OFF>
+__device__ __forceinline__ v4i_t ds_read_b128(uint32_t addr) {
+  v4i_t r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+
+// s_waitcnt lgkmcnt(N) tied to one 128-bit read result (as wait_lds_le).
+template <int N>
+__device__ __forceinline__ void wait_lds_le1(v4i_t& x) {
+  static_assert(N >= 0 && N < 16, "lgkmcnt range");
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(x) : "i"(N));
+}
+
 // Opaque re-definition of register values (no instruction is emitted).
 template <int N>
 __device__ __forceinline__ void launder(uint32_t (&x)[N]) {
@@ -155,8 +174,6 @@ __device__ __forceinline__ float max_xor32(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-constexpr int kVWin = 4;  // transposed V read pairs in flight
-
 // kRawMax: the scale is positive, so the running maximum is taken on raw
 // scores and the scale folds into the exponent's FMA; otherwise scores are
 // scaled first. BN: keys per tile, 64 (2 waves per SIMD) or 32 (half the
@@ -169,6 +186,8 @@ void prefill_kernel(PrefillArgs a) {
   constexpr int KT = BN / 16;                // 16-key score tiles per tile
   constexpr int KK = BN / 32;                // 32-key steps of the PV product
   constexpr int DU = BN / 16;                // 1 KiB DMA instructions per wave per K (or V) tile
+  constexpr int KW = 6;                      // K operand reads in flight in the score phase (64-key tiles)
+  constexpr int kVWin = 4;                   // transposed V read pairs in flight in the PV phase
   constexpr int kTileBytes = BN * kPD * 2;   // one K or V tile
   // Buffers of [K tile | V tile]: 3 for 32-key tiles (48 KiB, three
   // workgroups per CU, tiles fetched two ahead), 2 for 64-key tiles (64 KiB,
@@ -354,16 +373,44 @@ void prefill_kernel(PrefillArgs a) {
     for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) sacc[u][kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if constexpr (BN == 32) {
+      // 32-key tiles run at the register limit of three waves per SIMD, so
+      // the reads stay as the compiler schedules them.
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      uint4 kop[KT];
+      for (int ks = 0; ks < 4; ++ks) {
+        uint4 kop[KT];
 #pragma unroll
-      for (int kt = 0; kt < KT; ++kt) kop[kt] = *reinterpret_cast<const uint4*>(sK + kt * 16 * 256 + koff[ks]);
+        for (int kt = 0; kt < KT; ++kt) kop[kt] = *reinterpret_cast<const uint4*>(sK + kt * 16 * 256 + koff[ks]);
 #pragma unroll
-      for (int kt = 0; kt < KT; ++kt) {
-        sacc[0][kt] = mfma16x16x32(kop[kt], qop[0][ks], sacc[0][kt]);
-        sacc[1][kt] = mfma16x16x32(kop[kt], qop[1][ks], sacc[1][kt]);
+        for (int kt = 0; kt < KT; ++kt) {
+          sacc[0][kt] = mfma16x16x32(kop[kt], qop[0][ks], sacc[0][kt]);
+          sacc[1][kt] = mfma16x16x32(kop[kt], qop[1][ks], sacc[1][kt]);
+        }
       }
+    } else {
+      // K operand read j = ks * KT + kt feeds the two MFMAs of (ks, kt).
+      // The reads are issued KW ahead of their MFMAs, so each LDS latency is
+      // covered by the MFMAs of the reads before it instead of draining the
+      // queue before every k-step.
+      constexpr int NR = 4 * KT;
+      const uint32_t kbase = lds_addr(sK);
+      v4i_t kop[NR];
+      auto issue_k = [&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        kop[j] = ds_read_b128<(j % KT) * 16 * 256>(kbase + koff[j / KT]);
+      };
+      static_for<KW>([&](auto jc) { issue_k(jc); });
+      static_for<NR>([&](auto jc) {
+        constexpr int j = decltype(jc)::value, ks = j / KT, kt = j % KT;
+        constexpr int issued = j + KW < NR ? j + KW : NR;
+        wait_lds_le1<issued - j - 1>(kop[j]);
+        if constexpr (j + KW < NR) issue_k(Buf<j + KW>());
+        const uint4 a = __builtin_bit_cast(uint4, kop[j]);
+        sacc[0][kt] = mfma16x16x32(a, qop[0][ks], sacc[0][kt]);
+        sacc[1][kt] = mfma16x16x32(a, qop[1][ks], sacc[1][kt]);
+        // keep each read's MFMAs between its wait and the next one
+        __builtin_amdgcn_sched_barrier(0);
+      });
     }
 
     // ---- softmax numerators (each lane: one query, keys kt*16 + 4g + i) ----
