@@ -110,51 +110,6 @@ __device__ __forceinline__ void static_for(F&& f) { static_for_from<0, N>(f); }
 
 typedef int v2i_t __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
-}
-
-// ds_read_b64_tr_b16 at addr + OFF. Issued as inline assembly: the compiler's
-// own form of this read carries no aliasing information, so the compiler
-// would make it wait for every tile DMA in flight. Being opaque, it is not
-// counted by the compiler's waits either: results are only used after
-// wait_lds_le has covered them.
-template <int OFF>
-__device__ __forceinline__ v2i_t ds_read_tr_b64(uint32_t addr) {
-  v2i_t r;
-  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
-  return r;
-}
-
-// s_waitcnt lgkmcnt(N), tied to the registers it makes valid so that no use of
-// them is scheduled above it. Every LDS access issued after the reads being
-// waited for completes after them (LDS returns in order), so extra younger
-// accesses only make the wait stricter; no scalar memory load is issued
-// between these reads and their wait.
-template <int N>
-__device__ __forceinline__ void wait_lds_le(v2i_t& x, v2i_t& y) {
-  static_assert(N >= 0 && N < 16, "lgkmcnt range");
-  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(x), "+v"(y) : "i"(N));
-}
-
-typedef int v4i_t __attribute__((ext_vector_type(4)));
-
-// ds_read_b128 at addr + OFF, issued as inline assembly for the same reason
-// as the transposed reads: its result is used only after wait_lds_le1 has
-// covered it.
-template <int OFF>
-__device__ __forceinline__ v4i_t ds_read_b128(uint32_t addr) {
-  v4i_t r;
-  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
-  return r;
-}
-
-// s_waitcnt lgkmcnt(N) tied to one 128-bit read result (as wait_lds_le).
-template <int N>
-__device__ __forceinline__ void wait_lds_le1(v4i_t& x) {
-  static_assert(N >= 0 && N < 16, "lgkmcnt range");
-  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(x) : "i"(N));
-}
 
 // Opaque re-definition of register values (no instruction is emitted).
 template <int N>
@@ -174,6 +129,7 @@ __device__ __forceinline__ float max_xor32(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+
 // kRawMax: the scale is positive, so the running maximum is taken on raw
 // scores and the scale folds into the exponent's FMA; otherwise scores are
 // scaled first. BN: keys per tile, 64 (2 waves per SIMD) or 32 (half the
@@ -186,8 +142,6 @@ void prefill_kernel(PrefillArgs a) {
   constexpr int KT = BN / 16;                // 16-key score tiles per tile
   constexpr int KK = BN / 32;                // 32-key steps of the PV product
   constexpr int DU = BN / 16;                // 1 KiB DMA instructions per wave per K (or V) tile
-  constexpr int KW = 6;                      // K operand reads in flight in the score phase (64-key tiles)
-  constexpr int kVWin = 4;                   // transposed V read pairs in flight in the PV phase
   constexpr int kTileBytes = BN * kPD * 2;   // one K or V tile
   // Buffers of [K tile | V tile]: 3 for 32-key tiles (48 KiB, three
   // workgroups per CU, tiles fetched two ahead), 2 for 64-key tiles (64 KiB,
@@ -374,8 +328,6 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) sacc[u][kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     if constexpr (BN == 32) {
-      // 32-key tiles run at the register limit of three waves per SIMD, so
-      // the reads stay as the compiler schedules them.
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         uint4 kop[KT];
@@ -388,29 +340,26 @@ void prefill_kernel(PrefillArgs a) {
         }
       }
     } else {
-      // K operand read j = ks * KT + kt feeds the two MFMAs of (ks, kt).
-      // The reads are issued KW ahead of their MFMAs, so each LDS latency is
-      // covered by the MFMAs of the reads before it instead of draining the
-      // queue before every k-step.
+      // K operand read j = ks * KT + kt feeds the two MFMAs of (ks, kt); the
+      // reads are scheduled six ahead of their MFMAs (mask 0x100: LDS reads,
+      // 0x008: MFMA), where the compiler's own order drains the LDS queue
+      // before every k-step.
       constexpr int NR = 4 * KT;
-      const uint32_t kbase = lds_addr(sK);
-      v4i_t kop[NR];
-      auto issue_k = [&](auto jc) {
-        constexpr int j = decltype(jc)::value;
-        kop[j] = ds_read_b128<(j % KT) * 16 * 256>(kbase + koff[j / KT]);
-      };
-      static_for<KW>([&](auto jc) { issue_k(jc); });
-      static_for<NR>([&](auto jc) {
-        constexpr int j = decltype(jc)::value, ks = j / KT, kt = j % KT;
-        constexpr int issued = j + KW < NR ? j + KW : NR;
-        wait_lds_le1<issued - j - 1>(kop[j]);
-        if constexpr (j + KW < NR) issue_k(Buf<j + KW>());
-        const uint4 a = __builtin_bit_cast(uint4, kop[j]);
-        sacc[0][kt] = mfma16x16x32(a, qop[0][ks], sacc[0][kt]);
-        sacc[1][kt] = mfma16x16x32(a, qop[1][ks], sacc[1][kt]);
-        // keep each read's MFMAs between its wait and the next one
-        __builtin_amdgcn_sched_barrier(0);
-      });
+      uint4 kop[NR];
+#pragma unroll
+      for (int j = 0; j < NR; ++j) kop[j] = *reinterpret_cast<const uint4*>(sK + (j % KT) * 16 * 256 + koff[j / KT]);
+#pragma unroll
+      for (int j = 0; j < NR; ++j) {
+        sacc[0][j % KT] = mfma16x16x32(kop[j], qop[0][j / KT], sacc[0][j % KT]);
+        sacc[1][j % KT] = mfma16x16x32(kop[j], qop[1][j / KT], sacc[1][j % KT]);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+      for (int j = 0; j < NR - 6; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 12, 0);
     }
 
     // ---- softmax numerators (each lane: one query, keys kt*16 + 4g + i) ----
@@ -463,29 +412,37 @@ void prefill_kernel(PrefillArgs a) {
     }
 
     // ---- Oᵀ += Vᵀ Pᵀ, and the row sums (16 independent accumulators per k-step) ----
-    // Read pair j = 8 kk + dt (keys 32 kk + 0..15 and 16..31, dims 16 dt ..)
-    // is issued kVWin pairs ahead of its MFMAs.
-    const uint32_t vbase = lds_addr(sV);
-    v2i_t vlo[8 * KK], vhi[8 * KK];
-    auto issue_pair = [&](auto jc) {
-      constexpr int j = decltype(jc)::value, kk = j / 8, dt = j % 8;
-      vlo[j] = ds_read_tr_b64<kk * 32 * 256>(vbase + voff[dt]);
-      vhi[j] = ds_read_tr_b64<(kk * 32 + 16) * 256>(vbase + voff[dt]);
-    };
-    static_for<kVWin>([&](auto jc) { issue_pair(jc); });
-    static_for<8 * KK>([&](auto jc) {
-      constexpr int j = decltype(jc)::value, kk = j / 8, dt = j % 8;
-      constexpr int issued = j + kVWin < 8 * KK ? j + kVWin : 8 * KK;
-      wait_lds_le<2 * (issued - j - 1)>(vlo[j], vhi[j]);
-      if constexpr (j + kVWin < 8 * KK) issue_pair(Buf<j + kVWin>());
-      const uint4 vop = make_uint4(vlo[j].x, vlo[j].y, vhi[j].x, vhi[j].y);
-      oacc[0][dt] = mfma16x16x32(vop, pop[0][kk], oacc[0][dt]);
-      oacc[1][dt] = mfma16x16x32(vop, pop[1][kk], oacc[1][dt]);
-      if constexpr (dt == 7) {
-        oacc[0][8] = mfma16x16x32(ones, pop[0][kk], oacc[0][8]);
-        oacc[1][8] = mfma16x16x32(ones, pop[1][kk], oacc[1][8]);
+    // Read pair (kk, dt): keys 32 kk + 0..15 and 16..31, dims 16 dt .. 16 dt + 15.
+    // The LDS pointer is derived from this step's own stage array, so the
+    // compiler can tell these reads from the DMA in flight into the others.
+    typedef __attribute__((address_space(3))) const char lds_char_t;
+    lds_char_t* vl = (lds_char_t*)sV;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vl + kk * 32 * 256 + voff[dt]));
+        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vl + (kk * 32 + 16) * 256 + voff[dt]));
+        const v2i_t l2 = __builtin_bit_cast(v2i_t, lo), h2 = __builtin_bit_cast(v2i_t, hi);
+        const uint4 vop = make_uint4(l2.x, l2.y, h2.x, h2.y);
+        oacc[0][dt] = mfma16x16x32(vop, pop[0][kk], oacc[0][dt]);
+        oacc[1][dt] = mfma16x16x32(vop, pop[1][kk], oacc[1][dt]);
+        if (dt == 7) {
+          oacc[0][8] = mfma16x16x32(ones, pop[0][kk], oacc[0][8]);
+          oacc[1][8] = mfma16x16x32(ones, pop[1][kk], oacc[1][8]);
+        }
       }
-    });
+    if constexpr (BN == 64) {
+      // 64-key tiles: keep four read pairs ahead of their MFMAs (mask 0x100:
+      // LDS reads, 0x008: MFMA)
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
+#pragma unroll
+      for (int j = 0; j < 12; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 12, 1);
+    }
   };
   for (int tile = 0; tile < ntiles; tile += STAGES) {
     step(tile, Buf<0>());
