@@ -15,7 +15,7 @@ from workloads import configs, tensors
 pytestmark = pytest.mark.gpu
 
 
-def _run(wl, dev, seqs=None, split_waves=0, extra_check=None):
+def _run(wl, dev, seqs=None, split_waves=0, extra_check=None, scale=None):
     """store + decode on the GPU; the oracle repeats both on a host copy of the sampled sequences."""
     batch = tensors.materialize(wl, dev)
     seqs = list(range(wl.num_seqs)) if seqs is None else list(seqs)
@@ -23,7 +23,7 @@ def _run(wl, dev, seqs=None, split_waves=0, extra_check=None):
     k_new, v_new = tensors.to_u16(batch.k_new), tensors.to_u16(batch.v_new)
     q = tensors.to_u16(batch.q)
     slots = batch.slot_mapping.cpu().numpy()
-    scale = 1.0 / math.sqrt(wl.head_dim)
+    scale = 1.0 / math.sqrt(wl.head_dim) if scale is None else scale
     pa.pa_store_kvcache(batch.k_new, batch.v_new, batch.k_cache, batch.v_cache, batch.slot_mapping)
     out = pa.pa_decode(batch.q, batch.k_cache, batch.v_cache, batch.block_tables, batch.context_lens, scale,
                        wl.max_context_len, split_waves=split_waves)
@@ -129,3 +129,11 @@ def test_decode_block_permutation_invariant(dev):
     out2 = pa.pa_decode(batch.q, kc2, vc2, t2, batch.context_lens, 0.088, 1200)
     torch.cuda.synchronize()
     assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.05])
+def test_decode_nonpositive_scale(dev, scale):
+    # scale 0 gives the mean of the context's values; a negative scale weights low scores most
+    announce(f"decode scale {scale}")
+    _run(configs.config1(), dev, scale=scale)
+    _run(configs.config2(2), dev, seqs=range(0, 256, 17), split_waves=300, scale=scale)

@@ -15,14 +15,15 @@ from workloads import configs, tensors
 pytestmark = pytest.mark.gpu
 
 
-def _packed(wl, dev, causal=True, check_table_path=True, max_k=None):
+def _packed(wl, dev, causal=True, check_table_path=True, max_k=None, scale=None):
     """Prefill over packed q/k/v; the same keys read back through the cache must give identical bits.
 
     max_k overrides the max_seqlen_k hint, which only picks the key tile (1 -> 32 keys, 4096 -> 64 keys).
+    scale defaults to 1/sqrt(head_dim).
     """
     mk = wl.max_seqlen_k if max_k is None else max_k
     batch = tensors.materialize(wl, dev)
-    scale = 1.0 / math.sqrt(wl.head_dim)
+    scale = 1.0 / math.sqrt(wl.head_dim) if scale is None else scale
     pa.pa_store_kvcache(batch.k_new, batch.v_new, batch.k_cache, batch.v_cache, batch.slot_mapping)
     out = pa.pa_prefill_varlen(batch.q, batch.k_new, batch.v_new, batch.cu_seqlens_q, batch.cu_seqlens_k,
                                wl.max_seqlen_q, mk, scale, causal=causal)
@@ -90,6 +91,17 @@ def test_prefill_prefix_small(dev, block_size, group, max_k):
                                   block_size=block_size)
     _table(wl, dev, causal=True, max_k=max_k)
     _table(wl, dev, causal=False, max_k=max_k)
+
+
+@pytest.mark.parametrize("max_k", [1, 4096])
+@pytest.mark.parametrize("group", [1, 2, 4, 8])
+@pytest.mark.parametrize("scale", [0.0, -0.05])
+def test_prefill_nonpositive_scale(dev, group, scale, max_k):
+    # a scale <= 0 takes the kernel's other softmax form (scores scaled before the running maximum);
+    # scale 0 gives the mean of the visible values
+    announce(f"prefill scale {scale} G={group} max_k={max_k}")
+    wl = configs.prefill_workload("scale", [1, 17, 64, 65, 200], 0, 2 * group, 2, 64, seed=24)
+    _packed(wl, dev, causal=True, max_k=max_k, scale=scale)
 
 
 def test_prefill_empty_sequence_in_batch(dev):
