@@ -280,16 +280,16 @@ void prefill_kernel(PrefillArgs a) {
     const char* kb = reinterpret_cast<const char*>(a.k + krow0 + kvh * kPD);
     const char* vb = reinterpret_cast<const char*>(a.v + vrow0 + kvh * kPD);
     char* vdst = kdst + kTileBytes;
-    const int last = nk - 1 - t0;  // rows past it are clamped to it
+    const int last = nk - 1 - t0;  // rows past it are clamped to it (t0 < nk, so last >= 0)
+    // byte offsets from the tile's first row (below 2^31: checked on the host);
+    // a clamped row keeps its lane's swizzled chunk, selected without a branch
+    const uint32_t kcl = (uint32_t)(last * kstride * 2) + (((lane & 15) ^ (srow0 & 15)) << 4);
+    const uint32_t vcl = (uint32_t)(last * vstride * 2) + (((lane & 15) ^ ((srow0 & 7) << 1)) << 4);
 #pragma unroll
     for (int u = 0; u < DU; ++u) {
-      // byte offsets from the tile's first row (below 2^31: checked on the host)
-      uint32_t ko = (uint32_t)(16 * u * kstride * 2) + kofs;
-      uint32_t vo = (uint32_t)(16 * u * vstride * 2) + vofs;
-      if (last < kBN - 1 && srow0 + 16 * u > last) {
-        ko = (uint32_t)(last * kstride * 2) + (((lane & 15) ^ (srow0 & 15)) << 4);
-        vo = (uint32_t)(last * vstride * 2) + (((lane & 15) ^ ((srow0 & 7) << 1)) << 4);
-      }
+      const bool clamp = srow0 + 16 * u > last;
+      const uint32_t ko = clamp ? kcl : (uint32_t)(16 * u * kstride * 2) + kofs;
+      const uint32_t vo = clamp ? vcl : (uint32_t)(16 * u * vstride * 2) + vofs;
       const int o = (16 * u + 4 * wave) * 256;
       __builtin_amdgcn_global_load_lds(kb + ko, (lds_void_t*)(kdst + o), 16, 0, 0);
       __builtin_amdgcn_global_load_lds(vb + vo, (lds_void_t*)(vdst + o), 16, 0, 0);
@@ -312,7 +312,10 @@ void prefill_kernel(PrefillArgs a) {
     const int t0 = tile * kBN;
     if (STAGES > 2 && tile + 1 < ntiles) wait_vmem_le<2 * DU>(); else wait_vmem_le<0>();
     barrier_keep_loads();  // everyone's tile is in; everyone finished tile - 1
-    if (tile + STAGES - 1 < ntiles) issue_tile(t0 + (STAGES - 1) * kBN, buffer(Buf<(RB + STAGES - 1) % STAGES>()));
+    // The next DMA goes out before the score MFMAs with two stages (it has one
+    // tile to land), after them with three (two tiles to land), so that its
+    // issue overlaps the MFMAs in flight.
+    if (STAGES == 2 && tile + 1 < ntiles) issue_tile(t0 + kBN, buffer(Buf<(RB + 1) % STAGES>()));
     const char* sK = buffer(rb);
     const char* sV = sK + kTileBytes;
     // Re-define the per-lane LDS offsets at every step, so that the compiler
@@ -361,6 +364,9 @@ void prefill_kernel(PrefillArgs a) {
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 12, 0);
     }
+
+    if (STAGES > 2 && tile + STAGES - 1 < ntiles)
+      issue_tile(t0 + (STAGES - 1) * kBN, buffer(Buf<(RB + STAGES - 1) % STAGES>()));
 
     // ---- softmax numerators (each lane: one query, keys kt*16 + 4g + i) ----
     const bool need_mask = (t0 + kBN > full_below);
