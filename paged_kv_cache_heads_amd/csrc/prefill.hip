@@ -258,9 +258,14 @@ void prefill_kernel(PrefillArgs a) {
   // tbase + i (entries past the ones the sequence uses read as 0).
   const int nblk = a.block_table ? min(a.max_blocks_per_seq, (nk + a.block_size - 1) / max(a.block_size, 1)) : 0;
   int tbase = 0, tentry = 0;
+  // The load is waited for where it is issued (rarely: every 64 blocks), so
+  // that the compiler's wait bookkeeping never sees the entry pending at a
+  // later use; otherwise it drains all tile DMA in flight before every
+  // block lookup.
   auto load_table = [&](int base) {
     tbase = base;
     tentry = base + lane < nblk ? a.block_table[(int64_t)seq * a.max_blocks_per_seq + base + lane] : 0;
+    wait_vmem_le<0>();
   };
   if (a.block_table) load_table(0);
   int iblk = 0, ioff = 0;  // block and offset of the next tile to issue (tiles never straddle a block)
