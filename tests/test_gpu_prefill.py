@@ -104,6 +104,17 @@ def test_prefill_nonpositive_scale(dev, group, scale, max_k):
     _packed(wl, dev, causal=True, max_k=max_k, scale=scale)
 
 
+@pytest.mark.parametrize("max_k", [1, 8192])
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_table_past_64_blocks(dev, causal, max_k):
+    # 64-token blocks and a 4608-token cached prefix: the tables run past 64 entries, so the kernel
+    # reloads its cached table entries mid-sequence
+    announce(f"prefill table > 64 blocks causal={causal} max_k={max_k}")
+    wl = configs.prefill_workload("long-table", [300, 37], 4608, 4, 2, 96, seed=25, block_size=64)
+    assert wl.block_tables.shape[1] > 64
+    _table(wl, dev, causal=causal, max_k=max_k)
+
+
 def test_prefill_empty_sequence_in_batch(dev):
     announce("prefill with an empty sequence in the batch")
     wl = configs.prefill_workload("empty", [5, 0, 70], 0, 4, 2, 16, seed=23)
