@@ -110,7 +110,6 @@ __device__ __forceinline__ void static_for(F&& f) { static_for_from<0, N>(f); }
 
 typedef int v2i_t __attribute__((ext_vector_type(2)));
 
-
 // Opaque re-definition of register values (no instruction is emitted).
 template <int N>
 __device__ __forceinline__ void launder(uint32_t (&x)[N]) {
@@ -128,7 +127,6 @@ __device__ __forceinline__ float max_xor32(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-
 
 // kRawMax: the scale is positive, so the running maximum is taken on raw
 // scores and the scale folds into the exponent's FMA; otherwise scores are
