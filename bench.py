@@ -310,6 +310,34 @@ def cpu_baseline(batch, wl, budget_s=15.0):
                       f"({kv / 1e9:.3f} GB of K/V) in {elapsed:.1f} s, numpy fp64 with one BLAS thread"}
 
 
+def cpu_baseline_prefill(batch, wl, budget_s=10.0):
+    """The fp64 oracle's causal prefill on a bounded prefix of the varlen batch, on the host (TFLOP/s of
+    unmasked pairs, as the GPU figure)."""
+    import threadpoolctl
+
+    import oracle
+    from workloads import tensors
+
+    scale = 1.0 / math.sqrt(wl.head_dim)
+    q, k, v = tensors.to_u16(batch.q), tensors.to_u16(batch.k_new), tensors.to_u16(batch.v_new)
+    cu = np.asarray(wl.cu_seqlens_q, dtype=np.int64)
+    done, elapsed, flops = 0, 0.0, 0
+    with threadpoolctl.threadpool_limits(1):
+        while done < wl.num_seqs and elapsed < budget_s:
+            a, b = int(cu[done]), int(cu[done + 1])
+            n = b - a
+            one = np.array([0, n], dtype=np.int32)
+            t0 = time.perf_counter()
+            oracle.prefill_varlen(q[a:b], k[a:b], v[a:b], one, one, scale, causal=True)
+            elapsed += time.perf_counter() - t0
+            flops += n * (n + 1) // 2 * 4 * wl.head_dim * wl.num_q_heads
+            done += 1
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"causal prefill of the first {done} of {wl.num_seqs} sequences of the varlen batch "
+                      f"({flops / 1e9:.2f} GFLOP of unmasked pairs) in {elapsed:.1f} s, numpy fp64 with one "
+                      f"BLAS thread"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -497,6 +525,7 @@ def main():
         result["decode_graph"] = decode_graph_latency(pa, torch, b2, wl2, scale)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(b2, wl2)
+        result["cpu_baseline_prefill"] = cpu_baseline_prefill(b3, wl3)
     print(json.dumps(result), flush=True)
 
 
