@@ -1,0 +1,64 @@
+"""Host-side logic of bench.py: the work counts its rates divide by, the one-GPU guard and the oracle baseline."""
+
+import json
+import os
+import subprocess
+import sys
+
+import torch
+
+import bench
+from workloads import configs, tensors
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_refuses_more_than_one_gpu():
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                         text=True, timeout=120)
+    assert res.returncode == 2
+    msg = json.loads(res.stdout.strip().splitlines()[-1])
+    assert "error" in msg and msg["n_gpus"] == 2
+
+
+def test_decode_bytes_tiny_workload():
+    # context lengths 1, 37, 256, 300: 594 tokens, each a K and a V row of 8 heads x 128 bf16 values
+    wl = configs.config1()
+    b = bench.decode_bytes(wl)
+    assert b["kv"] == 594 * 8 * 128 * 2 * 2
+    q_out = 4 * 16 * 128 * 2 * 2
+    tables = (1 + 1 + 1 + 2) * 4  # ceil(L / 256) entries per sequence
+    assert b["total"] == b["kv"] + q_out + tables + 4 * 4
+
+
+def test_store_bytes():
+    wl = configs.config1()
+    # per token: K and V rows read and written (2 x 2 x 2048 bytes) and the 4-byte slot
+    assert bench.store_bytes(wl, 10) == 10 * (4 * 2048 + 4)
+
+
+def test_prefill_flops_counts_unmasked_pairs():
+    hq, d = 4, 128
+    wl = configs.prefill_workload("f", [1, 5], 0, hq, 2, 16, seed=1)
+    # causal, queries aligned with keys: n (n + 1) / 2 visible pairs per sequence
+    assert bench.prefill_flops(wl) == (1 + 15) * 4 * d * hq
+    assert bench.prefill_flops(wl, causal=False) == (1 + 25) * 4 * d * hq
+    wl = configs.prefill_workload("p", [3], 64, hq, 2, 16, seed=1, block_size=64)
+    # 3 queries after a 64-token prefix: each sees the prefix and the queries up to itself
+    assert bench.prefill_flops(wl) == (64 * 3 + 6) * 4 * d * hq
+    assert bench.prefill_flops(wl, causal=False) == 3 * 67 * 4 * d * hq
+
+
+def test_norm_rope_bytes():
+    wl = configs.config1()
+    heads = 16 + 2 * 8
+    per_token = heads * 128 * 2 * 2 + 128 * 4 + 8
+    assert bench.norm_rope_bytes(wl, 3) == 3 * per_token + 2 * 128 * 2
+
+
+def test_cpu_baseline_prefill_reports_the_oracle():
+    wl = configs.prefill_workload("cpu", [20, 7], 0, 16, 8, 16, seed=2)
+    batch = tensors.materialize(wl, torch.device("cpu"))
+    r = bench.cpu_baseline_prefill(batch, wl, budget_s=5.0)
+    assert r["kind"] == "oracle" and r["unit"] == "TFLOP/s" and r["cores"] == 1
+    assert r["value"] > 0 and "2 of 2 sequences" in r["sample"]
