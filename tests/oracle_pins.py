@@ -261,6 +261,23 @@ def check_key_shift_and_zero_scale(orc, seed=6):
     assert np.allclose(z[0, 0], _f64(vc[0, :, 0]).mean(axis=0), rtol=0, atol=1e-12)
 
 
+def check_negative_scale_is_negated_query(orc, seed=13):
+    # softmax(-s q.k) = softmax(s (-q).k): negating a bf16 query flips its sign bits, and the fp64 scores of
+    # the two forms are equal bit for bit, so decode and prefill give identical outputs
+    rng = np.random.default_rng(seed)
+    kc, vc, table, _, _ = _paged_case(rng, [5, 17], 2, 8, 4)
+    lens = np.array([5, 17])
+    q = _rand(rng, (2, 4, 8))
+    neg = q ^ np.uint16(0x8000)
+    assert np.array_equal(orc.decode(q, kc, vc, table, lens, -0.3), orc.decode(neg, kc, vc, table, lens, 0.3))
+    n = 6
+    qp, kp, vp = _rand(rng, (n, 4, 8)), _rand(rng, (n, 2, 8)), _rand(rng, (n, 2, 8))
+    cu = np.array([0, 2, n])
+    a = orc.prefill_varlen(qp, kp, vp, cu, cu, -0.3)
+    b = orc.prefill_varlen(qp ^ np.uint16(0x8000), kp, vp, cu, cu, 0.3)
+    assert np.array_equal(a, b)
+
+
 def check_zero_context(orc, seed=7):
     rng = np.random.default_rng(seed)
     kc, vc = _rand(rng, (2, 4, 1, 4)), _rand(rng, (2, 4, 1, 4))
@@ -405,7 +422,7 @@ ALL_CHECKS = [
     check_bf16_widen, check_golden_store, check_golden_decode, check_golden_prefill,
     check_slot_of, check_store_bruteforce, check_contiguous_equals_paged, check_permutation_invariance,
     check_identical_keys_mean, check_one_token, check_two_token_closed_form,
-    check_key_shift_and_zero_scale, check_zero_context, check_gqa_mapping, check_g1_is_mha,
+    check_key_shift_and_zero_scale, check_negative_scale_is_negated_query, check_zero_context, check_gqa_mapping, check_g1_is_mha,
     check_prefill_last_row_is_decode, check_prefix_rows_equal_full, check_against_sdpa,
     check_against_bruteforce,
 ]
