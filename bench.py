@@ -282,6 +282,11 @@ def decode_graph_latency(pa, torch, b2, wl2, scale, batches=(1, 16, 256), iters=
     return res
 
 
+def _host_cores() -> dict:
+    """The host's core counts beside the one thread the oracle runs on."""
+    return {"host_cores_available": len(os.sched_getaffinity(0)), "host_cpu_count": os.cpu_count()}
+
+
 def cpu_baseline(batch, wl, budget_s=15.0):
     """The fp64 oracle on a bounded prefix of the decode batch, on the host."""
     import threadpoolctl
@@ -305,7 +310,7 @@ def cpu_baseline(batch, wl, budget_s=15.0):
             elapsed += time.perf_counter() - t0
             kv += int(wl.context_lens[seqs].astype(np.int64).sum()) * wl.num_kv_heads * wl.head_dim * 4
             done = seqs[-1] + 1
-    return {"value": kv / elapsed / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+    return {"value": kv / elapsed / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle", **_host_cores(),
             "sample": f"store + decode of the first {done} of {wl.num_seqs} sequences of the decode batch "
                       f"({kv / 1e9:.3f} GB of K/V) in {elapsed:.1f} s, numpy fp64 with one BLAS thread"}
 
@@ -332,7 +337,7 @@ def cpu_baseline_prefill(batch, wl, budget_s=10.0):
             elapsed += time.perf_counter() - t0
             flops += n * (n + 1) // 2 * 4 * wl.head_dim * wl.num_q_heads
             done += 1
-    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle", **_host_cores(),
             "sample": f"causal prefill of the first {done} of {wl.num_seqs} sequences of the varlen batch "
                       f"({flops / 1e9:.2f} GFLOP of unmasked pairs) in {elapsed:.1f} s, numpy fp64 with one "
                       f"BLAS thread"}
