@@ -282,6 +282,27 @@ def decode_graph_latency(pa, torch, b2, wl2, scale, batches=(1, 16, 256), iters=
     return res
 
 
+def cold_launches(torch, dev, kernels, calls, reps=10):
+    """Median event-timed duration (us) of each launch run alone after a 512 MiB write has flushed the L2
+    and MALL, so that no kernel finds its inputs left in cache by the one before it."""
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    out = {}
+    for name in kernels:
+        t = []
+        for r in range(reps + 2):
+            flush.fill_(r & 0xFF)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            calls[name]()
+            e1.record()
+            torch.cuda.synchronize()
+            if r >= 2:
+                t.append(e0.elapsed_time(e1) * 1e3)
+        out[name] = round(float(np.median(t)), 2)
+    del flush
+    return out
+
+
 def _host_cores() -> dict:
     """The host's core counts beside the one thread the oracle runs on."""
     return {"host_cores_available": len(os.sched_getaffinity(0)), "host_cpu_count": os.cpu_count()}
@@ -446,6 +467,8 @@ def main():
         stats[name] = {"median": round(float(np.median(t)), 2), "min": round(float(np.min(t)), 2),
                        "max": round(float(np.max(t)), 2)}
     peaks = measured_peaks(torch, dev)
+    # after the timed steps: each launch alone with the caches flushed first (a 512 MiB write, untimed)
+    cold = cold_launches(torch, dev, kernels, calls)
 
     dbytes = decode_bytes(wl2)
     leg_bytes = dbytes["total"] + store_bytes(wl2, wl2.num_seqs)  # the decode plus the new tokens' store
@@ -507,6 +530,7 @@ def main():
                              "bytes_per_launch": smp_bytes, "avg_launch_us": round(ms["sample_decode"] * 1e3, 2)},
         "kernels_us": {k: round(v * 1e3, 2) for k, v in ms.items()},
         "kernels_us_stats": stats,
+        "kernels_us_cold": cold,
         "measured_peaks": peaks,
         "store_GBs": {k: round(sb[k] / (ms[k] * 1e-3) / 1e9, 1) for k in sb},
         "roofline_store": {k: {"bound": "hbm", "kernel": "store_tokens_kernel (%s batch)" % (
