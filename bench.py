@@ -467,8 +467,9 @@ def main():
         stats[name] = {"median": round(float(np.median(t)), 2), "min": round(float(np.min(t)), 2),
                        "max": round(float(np.max(t)), 2)}
     peaks = measured_peaks(torch, dev)
-    # after the timed steps: each launch alone with the caches flushed first (a 512 MiB write, untimed)
-    cold = cold_launches(torch, dev, kernels, calls)
+    # after the timed steps: each launch alone with the caches flushed first (a 512 MiB write, untimed);
+    # skipped in profiling runs, whose per-kernel statistics cover the timed steps only
+    cold = None if args.step_only else cold_launches(torch, dev, kernels, calls)
 
     dbytes = decode_bytes(wl2)
     leg_bytes = dbytes["total"] + store_bytes(wl2, wl2.num_seqs)  # the decode plus the new tokens' store
