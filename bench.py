@@ -375,7 +375,7 @@ def main():
                     help="also time store + decode of the long-context batch (512 seqs, Hq 32, L log-uniform "
                          "256..32768, 164,794-block pool; about 14 GB of K/V per step), reported beside the line")
     ap.add_argument("--step-only", action="store_true",
-                    help="skip the untimed host block-manager and decode-graph legs (profiling runs)")
+                    help="skip the untimed host block-manager, decode-graph and cold-launch legs (profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, run one 256 MiB device copy (reads and writes a known byte count) "
                          "so that profiler byte counters can be calibrated against it")
