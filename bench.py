@@ -1,21 +1,25 @@
 """Benchmark of the paged-KV-cache attention path on one MI355X.
 
 One step is one pass of the whole path over seeded synthetic batches:
-  decode leg   store 256 new tokens + paged decode (256 seqs, L ~ U{100..2048},
-               Hq 16 / Hkv 8 / D 128, 256-token blocks, 4096-block pool), one
-               pa_store_decode launch (the separate pa_store_kvcache +
-               pa_decode calls are timed after the steps and reported beside);
-  prefill leg  store + causal varlen prefill over packed q/k/v (about 29 seqs
-               of 100..1024 tokens, at most 16384 tokens);
-  prefix leg   store + prefix-cached prefill through the block table (32 seqs
-               sharing 1024 cached tokens, 128..512 new tokens each);
-  fused leg    QK-RMSNorm + rotary embedding + store of the prefill batch's
-               q/k/v (one pass, reported as its own roofline);
-  sampler leg  Gumbel-max sampling of one token for each of the 256 decode
-               sequences over a 151936-token vocabulary (fp32 logits).
-After the timed steps (outside them): the decode leg as two separate calls,
-host timings of the C++ block manager, and the wall-clock decode-step latency
-eager vs graph-captured at batch 1, 16 and 256.
+  decode leg       store 256 new tokens + paged decode (256 seqs, L ~ U{100..2048},
+                   Hq 16 / Hkv 8 / D 128, 256-token blocks, 4096-block pool), one
+                   pa_store_decode call (the separate pa_store_kvcache + pa_decode
+                   calls are timed after the steps and reported beside);
+  long decode leg  the same step for the long-context batch: 512 seqs, Hq 32 / Hkv 8
+                   (G = 4), L log-uniform in [256, 32768], a 164,794-block pool
+                   (60% of HBM for one layer's K and V); the split-K decode;
+  prefill leg      store + causal varlen prefill over packed q/k/v (about 29 seqs
+                   of 100..1024 tokens, at most 16384 tokens);
+  prefix leg       store + prefix-cached prefill through the block table (32 seqs
+                   sharing 1024 cached tokens, 128..512 new tokens each);
+  fused leg        QK-RMSNorm + rotary embedding + store of the prefill batch's
+                   q/k/v (one pass, reported as its own roofline);
+  sampler leg      Gumbel-max sampling of one token for each of the 256 decode
+                   sequences over a 151936-token vocabulary (fp32 logits).
+After the timed steps (outside them): the decode legs as two separate calls,
+host timings of the C++ block manager, the wall-clock decode-step latency eager
+vs graph-captured at batch 1, 16 and 256, and the fp64 oracle timed on the
+host's cores over the decode, prefill, prefix and long-decode batches.
 Inputs are resident in HBM before timing starts. `value` is the decode leg's
 KV-read throughput (bytes of K and V the decode must read, over the leg's
 time); the prefill legs report TFLOP/s of unmasked query-key pairs. Kernel
@@ -42,6 +46,12 @@ METRIC = "paged decode attn KV-read GB/s (% HBM peak); prefill attn TFLOP/s (% M
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 SAMPLER_VOCAB = 151936          # vocabulary of the Qwen3 family the pages benchmark
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+# The pages' end-to-end figure, quoted as context (other hardware, whole engine, not this path's metric):
+# nano-vLLM offline generation of Qwen3-0.6B over 256 random-length requests on a laptop RTX 4070
+# (page "nano-vLLM 最小化vLLM重新实现", 基准测试).
+PAGES_END_TO_END = {"value": 1434, "unit": "tok/s", "model": "Qwen3-0.6B", "sequences": 256,
+                    "hardware": "RTX 4070 laptop GPU", "what": "whole-engine offline generation, 133,966 tokens "
+                    "in 93.41 s; context only, not comparable with this path's kernel metric"}
 
 
 def decode_bytes(wl) -> dict:
@@ -78,71 +88,31 @@ def prefill_flops(wl, causal=True) -> int:
     return pairs * 4 * wl.head_dim * wl.num_q_heads
 
 
-def separate_decode_leg(pa, torch, b2, wl2, scale, mk2, ws, out2, args):
-    """The decode leg as pa_store_kvcache + pa_decode (two launches), median over the step count."""
+def separate_decode_leg(pa, torch, b, wl, scale, max_len, ws, out, steps, warmup, split_waves=0):
+    """A decode leg as pa_store_kvcache + pa_decode (two launches), median over the step count."""
     def once(ev=None):
         if ev is not None:
             ev[0].record()
-        pa.pa_store_kvcache(b2.k_new, b2.v_new, b2.k_cache, b2.v_cache, b2.slot_mapping)
+        pa.pa_store_kvcache(b.k_new, b.v_new, b.k_cache, b.v_cache, b.slot_mapping)
         if ev is not None:
             ev[1].record()
-        pa.pa_decode(b2.q, b2.k_cache, b2.v_cache, b2.block_tables, b2.context_lens, scale, mk2, out=out2,
-                     workspace=ws, split_waves=args.split_waves)
+        pa.pa_decode(b.q, b.k_cache, b.v_cache, b.block_tables, b.context_lens, scale, max_len, out=out,
+                     workspace=ws, split_waves=split_waves)
         if ev is not None:
             ev[2].record()
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         once()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     for e in evs:
         once(e)
     torch.cuda.synchronize()
     st = float(np.median([e[0].elapsed_time(e[1]) for e in evs]))
     dt = float(np.median([e[1].elapsed_time(e[2]) for e in evs]))
-    kv = decode_bytes(wl2)["kv"]
+    kv = decode_bytes(wl)["kv"]
     return {"store_us": round(st * 1e3, 2), "decode_us": round(dt * 1e3, 2),
             "kv_GBs_leg": round(kv / ((st + dt) * 1e-3) / 1e9, 1),
-            "decode_GBs": round(decode_bytes(wl2)["total"] / (dt * 1e-3) / 1e9, 1)}
-
-
-def long_decode(pa, torch, dev, steps=10, warmup=3):
-    """Store + decode of the long-context batch: 512 sequences, Hq 32 / Hkv 8 (G = 4), L log-uniform in
-    [256, 32768], a 164,794-block pool (60% of HBM for one layer's K and V)."""
-    from workloads import configs, tensors
-    wl5 = configs.config5()
-    b5 = tensors.materialize(wl5, dev, fill_nan=False)
-    scale = 1.0 / math.sqrt(wl5.head_dim)
-    ws = torch.empty(pa.pa_decode_workspace_size(wl5.num_seqs, 32, 8, 128, wl5.max_context_len),
-                     dtype=torch.uint8, device=dev)
-    out = torch.empty((wl5.num_seqs, 32, 128), dtype=torch.bfloat16, device=dev)
-    store = lambda: pa.pa_store_kvcache(b5.k_new, b5.v_new, b5.k_cache, b5.v_cache, b5.slot_mapping)  # noqa: E731
-    dec = lambda: pa.pa_decode(b5.q, b5.k_cache, b5.v_cache, b5.block_tables, b5.context_lens, scale,  # noqa: E731
-                               wl5.max_context_len, out=out, workspace=ws)
-    for _ in range(warmup):
-        store()
-        dec()
-    torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    for e in ev:
-        e[0].record()
-        store()
-        e[1].record()
-        dec()
-        e[2].record()
-    torch.cuda.synchronize()
-    st = float(np.median([e[0].elapsed_time(e[1]) for e in ev]))
-    dt = float(np.median([e[1].elapsed_time(e[2]) for e in ev]))
-    db = decode_bytes(wl5)
-    res = {"workload": "decode step of 512 seqs, context log-uniform 256..32768 (Hq 32, Hkv 8, D 128, "
-                       "256-token blocks, 164,794-block pool)",
-           "kv_bytes": db["kv"], "store_us": round(st * 1e3, 2), "decode_us": round(dt * 1e3, 2),
-           "kv_GBs_step": round(db["kv"] / ((st + dt) * 1e-3) / 1e9, 1),
-           "decode_GBs": round(db["total"] / (dt * 1e-3) / 1e9, 1),
-           "frac": round(db["total"] / (dt * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "split_waves":
-               pa.pa_decode_split_waves(wl5.num_seqs, 32, 8, wl5.max_context_len)}
-    del b5, ws, out
-    torch.cuda.empty_cache()
-    return res
+            "decode_GBs": round(decode_bytes(wl)["total"] / (dt * 1e-3) / 1e9, 1)}
 
 
 def measured_peaks(torch, dev):
@@ -175,26 +145,33 @@ def measured_peaks(torch, dev):
             "note": "1 GiB device copy (read + write bytes); torch.matmul bf16 8192^3; best of 10"}
 
 
-def measured_traffic():
-    """HBM bytes per pa_decode launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
-    summary, or None if the decode kernel source or the compile flags changed since the
-    counters were taken."""
+def decode_source_sha() -> str:
+    """Hash of the decode kernels' sources and build flags: a recorded counter figure is only
+    reported while it still describes the code being run."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "bench_default_hbm_traffic.md")
     srcs = [os.path.join(ROOT, "paged_kv_cache_heads_amd", "csrc", n) for n in ("decode.hip", "common.h")]
     srcs.append(os.path.join(ROOT, "paged_kv_cache_heads_amd", "build.py"))
+    return hashlib.sha256(b"".join(open(p, "rb").read() for p in srcs)).hexdigest()[:16]
+
+
+def measured_traffic(leg: str):
+    """HBM bytes per launch of a decode leg ("decode" or "long_decode") from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE summary, or None if the decode kernel sources or the compile flags changed
+    since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "bench_default_hbm_traffic.md")
     try:
-        rec = None
+        recs = []
         with open(path, encoding="utf-8") as f:
             for line in f:
                 if line.startswith("traffic_json:"):
-                    rec = json.loads(line.split(":", 1)[1])
-        sha = hashlib.sha256(b"".join(open(p, "rb").read() for p in srcs)).hexdigest()[:16]
+                    recs.append(json.loads(line.split(":", 1)[1]))
+        sha = decode_source_sha()
     except OSError:
         return None
-    if not rec or rec.get("source_sha256_16") != sha:
-        return None
-    return rec["bytes_per_launch"]
+    for rec in recs:
+        if rec.get("leg") == leg and rec.get("source_sha256_16") == sha:
+            return rec["bytes_per_launch"]
+    return None
 
 
 def host_block_manager(wl2, wl4, reps=20):
@@ -303,65 +280,140 @@ def cold_launches(torch, dev, kernels, calls, reps=10):
     return out
 
 
-def _host_cores() -> dict:
-    """The host's core counts beside the one thread the oracle runs on."""
-    return {"host_cores_available": len(os.sched_getaffinity(0)), "host_cpu_count": os.cpu_count()}
+# ----------------------------------------------------------------------------- oracle baseline (host)
+#
+# The fp64 oracle as it stands, timed on the host's cores. Its work is Python loops over positions,
+# sequences and heads around small numpy calls, which threads cannot share, so the cores are used the
+# way an unmodified single-threaded program can use them: one worker process per core (BLAS limited
+# to one thread each), each running the oracle over its own share of the sequences. The pool is
+# spawned before anything touches the GPU; each worker times only its oracle calls, and the rate is
+# the shares' total work over the slowest worker's time.
 
 
-def cpu_baseline(batch, wl, budget_s=15.0):
-    """The fp64 oracle on a bounded prefix of the decode batch, on the host."""
+def host_cores() -> int:
+    return len(os.sched_getaffinity(0))
+
+
+def start_oracle_pool(n: int):
+    import multiprocessing as mp
+    pool = mp.get_context("spawn").Pool(n)
+    pool.map(_worker_ready, range(n))  # every worker has started (and imported numpy) before timing
+    return pool
+
+
+def _worker_ready(_):
+    return os.getpid()
+
+
+def _oracle_worker(task: dict) -> float:
+    """One share of an oracle baseline, in a worker process: seconds spent in the oracle calls."""
     import threadpoolctl
 
     import oracle
+    with threadpoolctl.threadpool_limits(1):
+        t0 = time.perf_counter()
+        if task["kind"] == "decode":
+            kc, vc = oracle.store_kvcache(task["k_new"], task["v_new"], task["slots"], task["k"], task["v"])
+            oracle.decode(task["q"], kc, vc, task["tables"], task["lens"], task["scale"])
+        else:
+            oracle.prefill_varlen(task["q"], task["k"], task["v"], task["cu_q"], task["cu_k"], task["scale"],
+                                  causal=True, block_table=task.get("tables"))
+        return time.perf_counter() - t0
+
+
+def balanced_shares(costs, n: int):
+    """Indices split into at most n groups of about equal total cost (heaviest first to the lightest)."""
+    groups, load = [[] for _ in range(n)], [0] * n
+    for i in sorted(range(len(costs)), key=lambda i: -costs[i]):
+        j = min(range(n), key=load.__getitem__)
+        groups[j].append(i)
+        load[j] += costs[i]
+    return [sorted(g) for g in groups if g]
+
+
+def decode_tasks(batch, wl, seqs, n: int):
+    """Store + decode of the given sequences, split in n shares, each with a host copy of its blocks."""
     from tests.parity import Compact  # test infrastructure, used only for this leg
     from workloads import tensors
 
-    scale = 1.0 / math.sqrt(wl.head_dim)
-    q = tensors.to_u16(batch.q)
-    k_new, v_new = tensors.to_u16(batch.k_new), tensors.to_u16(batch.v_new)
+    q, k_new, v_new = tensors.to_u16(batch.q), tensors.to_u16(batch.k_new), tensors.to_u16(batch.v_new)
     slots = batch.slot_mapping.cpu().numpy()
-    done, elapsed, kv = 0, 0.0, 0
-    with threadpoolctl.threadpool_limits(1):
-        while done < wl.num_seqs and elapsed < budget_s:
-            seqs = list(range(done, min(done + 8, wl.num_seqs)))
-            host = Compact(batch, seqs)
-            t0 = time.perf_counter()
-            host.store(k_new, v_new, slots, wl.block_size)
-            oracle.decode(q[seqs], host.k, host.v, host.tables, wl.context_lens[seqs], scale)
-            elapsed += time.perf_counter() - t0
-            kv += int(wl.context_lens[seqs].astype(np.int64).sum()) * wl.num_kv_heads * wl.head_dim * 4
-            done = seqs[-1] + 1
-    return {"value": kv / elapsed / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle", **_host_cores(),
-            "sample": f"store + decode of the first {done} of {wl.num_seqs} sequences of the decode batch "
-                      f"({kv / 1e9:.3f} GB of K/V) in {elapsed:.1f} s, numpy fp64 with one BLAS thread"}
+    lens = wl.context_lens.astype(np.int64)
+    tasks, work = [], []
+    for share in balanced_shares([int(lens[s]) for s in seqs], n):
+        ss = [int(seqs[i]) for i in share]
+        host = Compact(batch, ss)
+        tasks.append({"kind": "decode", "q": q[ss], "k_new": k_new[ss], "v_new": v_new[ss],
+                      "slots": np.array([host.remap_slot(int(slots[s]), wl.block_size) for s in ss], np.int64),
+                      "k": host.k, "v": host.v, "tables": host.tables, "lens": lens[ss],
+                      "scale": 1.0 / math.sqrt(wl.head_dim)})
+        work.append(int(lens[ss].sum()) * wl.num_kv_heads * wl.head_dim * 4)
+    return tasks, work
 
 
-def cpu_baseline_prefill(batch, wl, budget_s=10.0):
-    """The fp64 oracle's causal prefill on a bounded prefix of the varlen batch, on the host (TFLOP/s of
-    unmasked pairs, as the GPU figure)."""
-    import threadpoolctl
-
-    import oracle
+def prefill_tasks(batch, wl, n: int, paged: bool):
+    """Causal prefill of every sequence, split in n shares: packed q/k/v slices, or (paged) the
+    queries with a host copy of the blocks their tables name (the new tokens already stored)."""
+    from tests.parity import Compact  # test infrastructure, used only for this leg
     from workloads import tensors
 
-    scale = 1.0 / math.sqrt(wl.head_dim)
-    q, k, v = tensors.to_u16(batch.q), tensors.to_u16(batch.k_new), tensors.to_u16(batch.v_new)
-    cu = np.asarray(wl.cu_seqlens_q, dtype=np.int64)
-    done, elapsed, flops = 0, 0.0, 0
-    with threadpoolctl.threadpool_limits(1):
-        while done < wl.num_seqs and elapsed < budget_s:
-            a, b = int(cu[done]), int(cu[done + 1])
-            n = b - a
-            one = np.array([0, n], dtype=np.int32)
-            t0 = time.perf_counter()
-            oracle.prefill_varlen(q[a:b], k[a:b], v[a:b], one, one, scale, causal=True)
-            elapsed += time.perf_counter() - t0
-            flops += n * (n + 1) // 2 * 4 * wl.head_dim * wl.num_q_heads
-            done += 1
-    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle", **_host_cores(),
-            "sample": f"causal prefill of the first {done} of {wl.num_seqs} sequences of the varlen batch "
-                      f"({flops / 1e9:.2f} GFLOP of unmasked pairs) in {elapsed:.1f} s, numpy fp64 with one "
-                      f"BLAS thread"}
+    q = tensors.to_u16(batch.q)
+    k = v = None
+    if not paged:
+        k, v = tensors.to_u16(batch.k_new), tensors.to_u16(batch.v_new)
+    cq, ck = wl.cu_seqlens_q.astype(np.int64), wl.cu_seqlens_k.astype(np.int64)
+    nq, nk = np.diff(cq), np.diff(ck)
+    pairs = [int((b - a) * a + a * (a + 1) // 2) for a, b in zip(nq, nk)]
+    tasks, work = [], []
+    for share in balanced_shares(pairs, n):
+        rows = np.concatenate([np.arange(cq[i], cq[i + 1]) for i in share])
+        cu_q = np.concatenate([[0], np.cumsum(nq[share])]).astype(np.int32)
+        cu_k = np.concatenate([[0], np.cumsum(nk[share])]).astype(np.int32)
+        task = {"kind": "prefill", "q": q[rows], "cu_q": cu_q, "cu_k": cu_k, "scale": 1.0 / math.sqrt(wl.head_dim)}
+        if paged:
+            host = Compact(batch, share)
+            task.update(k=host.k, v=host.v, tables=host.tables)
+        else:
+            krows = np.concatenate([np.arange(ck[i], ck[i + 1]) for i in share])
+            task.update(k=k[krows], v=v[krows])
+        tasks.append(task)
+        work.append(sum(pairs[i] for i in share) * 4 * wl.head_dim * wl.num_q_heads)
+    return tasks, work
+
+
+def run_oracle_baseline(pool, tasks, work, unit: str, sample: str) -> dict:
+    secs = pool.map(_oracle_worker, tasks, chunksize=1)
+    total, slowest = float(sum(work)), max(secs)
+    scale = 1e9 if unit == "GB/s" else 1e12
+    return {"value": total / slowest / scale, "unit": unit, "cores": len(tasks), "kind": "oracle",
+            "host_cores_available": host_cores(), "host_cpu_count": os.cpu_count(),
+            "oracle_s_slowest_share": round(slowest, 3), "oracle_s_all_shares": round(float(sum(secs)), 3),
+            "sample": sample + f"; numpy fp64, {len(tasks)} worker processes with one BLAS thread each"}
+
+
+def cpu_baselines(pool, n, b2, wl2, b3, wl3, b4, wl4, b5, wl5, long_sample: int = 128) -> dict:
+    """Oracle baselines for the decode, prefill, prefix and long-decode batches (each leg's own unit)."""
+    res = {}
+    tasks, work = decode_tasks(b2, wl2, list(range(wl2.num_seqs)), n)
+    res["cpu_baseline"] = run_oracle_baseline(
+        pool, tasks, work, "GB/s", f"store + decode of all {wl2.num_seqs} sequences of the decode batch "
+        f"({sum(work) / 1e9:.3f} GB of K/V)")
+    tasks, work = prefill_tasks(b3, wl3, n, paged=False)
+    res["cpu_baseline_prefill"] = run_oracle_baseline(
+        pool, tasks, work, "TFLOP/s", f"causal prefill of all {wl3.num_seqs} sequences of the varlen batch "
+        f"({sum(work) / 1e9:.2f} GFLOP of unmasked pairs)")
+    tasks, work = prefill_tasks(b4, wl4, n, paged=True)
+    res["cpu_baseline_prefix_prefill"] = run_oracle_baseline(
+        pool, tasks, work, "TFLOP/s", f"prefix-cached prefill of all {wl4.num_seqs} sequences through their "
+        f"block tables ({sum(work) / 1e9:.2f} GFLOP of unmasked pairs)")
+    if b5 is not None:
+        seqs = sorted(np.random.default_rng(505).choice(wl5.num_seqs, min(long_sample, wl5.num_seqs),
+                                                        replace=False).tolist())
+        tasks, work = decode_tasks(b5, wl5, seqs, n)
+        res["cpu_baseline_long_decode"] = run_oracle_baseline(
+            pool, tasks, work, "GB/s", f"store + decode of {len(seqs)} of the {wl5.num_seqs} long-context "
+            f"sequences, drawn uniformly with seed 505 ({sum(work) / 1e9:.3f} GB of K/V)")
+    return res
 
 
 def main():
@@ -371,9 +423,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--split-waves", type=int, default=0, help="decode work split (0 = library choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--long-decode", action="store_true",
-                    help="also time store + decode of the long-context batch (512 seqs, Hq 32, L log-uniform "
-                         "256..32768, 164,794-block pool; about 14 GB of K/V per step), reported beside the line")
+    ap.add_argument("--no-long-decode", action="store_true",
+                    help="leave the long-context decode leg (161 GiB pool, about 14 GB of K/V per step) out of the step")
     ap.add_argument("--step-only", action="store_true",
                     help="skip the untimed host block-manager, decode-graph and cold-launch legs (profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -386,6 +437,19 @@ def main():
                           "n_gpus": args.gpus}))
         sys.exit(2)
 
+    # the oracle's worker processes start before anything touches the GPU
+    n_cores = host_cores()
+    pool = None if args.no_cpu_baseline else start_oracle_pool(n_cores)
+    try:
+        result = run(args, pool, n_cores)
+    finally:
+        if pool is not None:
+            pool.terminate()
+            pool.join()
+    print(json.dumps(result), flush=True)
+
+
+def run(args, pool, n_cores) -> dict:
     import torch
 
     import paged_kv_cache_heads_amd as pa
@@ -405,6 +469,16 @@ def main():
     out3 = torch.empty((wl3.num_tokens, 16, 128), dtype=torch.bfloat16, device=dev)
     out4 = torch.empty((wl4.num_tokens, 16, 128), dtype=torch.bfloat16, device=dev)
     mq3, mq4, mk2 = wl3.max_seqlen_q, wl4.max_seqlen_q, wl2.max_context_len
+    # long-context batch: the pool is 60% of HBM for one layer's K and V; rows no sequence holds are
+    # zero-filled (the parity tests fill them with NaN), to keep the set-up short
+    wl5 = b5 = ws5 = out5 = None
+    if not args.no_long_decode:
+        wl5 = configs.config5()
+        b5 = tensors.materialize(wl5, dev, fill_nan=False)
+        mk5 = wl5.max_context_len
+        ws5 = torch.empty(max(pa.pa_decode_workspace_size(wl5.num_seqs, 32, 8, 128, mk5, args.split_waves), 16),
+                          dtype=torch.uint8, device=dev)
+        out5 = torch.empty((wl5.num_seqs, 32, 128), dtype=torch.bfloat16, device=dev)
     from workloads import rope
     nr_rng = np.random.default_rng(7)
     nr_qw = torch.as_tensor(rope.norm_weight(nr_rng, 128).view(np.int16)).to(dev).view(torch.bfloat16)
@@ -420,19 +494,24 @@ def main():
     smp_tokens = torch.empty(wl2.num_seqs, dtype=torch.int32, device=dev)
     smp_ws = torch.empty(pa.pa_sample_workspace_size(wl2.num_seqs, SAMPLER_VOCAB), dtype=torch.uint8, device=dev)
 
-    kernels = ["decode", "store_prefill", "prefill", "store_prefix", "prefill_prefix",
+    kernels = ["decode", "long_decode", "store_prefill", "prefill", "store_prefix", "prefill_prefix",
                "norm_rope_prefill", "sample_decode"]
+    if b5 is None:
+        kernels.remove("long_decode")
     calls = {
         "decode": lambda: pa.pa_store_decode(b2.q, b2.k_new, b2.v_new, b2.k_cache, b2.v_cache, b2.block_tables,
                                              b2.context_lens, scale, mk2, out=out2, workspace=ws,
                                              split_waves=args.split_waves),
+        "long_decode": lambda: pa.pa_store_decode(b5.q, b5.k_new, b5.v_new, b5.k_cache, b5.v_cache,
+                                                  b5.block_tables, b5.context_lens, scale, wl5.max_context_len,
+                                                  out=out5, workspace=ws5, split_waves=args.split_waves),
         "store_prefill": lambda: pa.pa_store_kvcache(b3.k_new, b3.v_new, b3.k_cache, b3.v_cache, b3.slot_mapping),
         "prefill": lambda: pa.pa_prefill_varlen(b3.q, b3.k_new, b3.v_new, b3.cu_seqlens_q, b3.cu_seqlens_k, mq3,
                                                 wl3.max_seqlen_k, scale, out=out3),
         "store_prefix": lambda: pa.pa_store_kvcache(b4.k_new, b4.v_new, b4.k_cache, b4.v_cache, b4.slot_mapping),
         "prefill_prefix": lambda: pa.pa_prefill_varlen(b4.q, b4.k_cache, b4.v_cache, b4.cu_seqlens_q,
-                                                       b4.cu_seqlens_k, mq4, wl4.max_seqlen_k, scale, block_table=b4.block_tables,
-                                                       out=out4),
+                                                       b4.cu_seqlens_k, mq4, wl4.max_seqlen_k, scale,
+                                                       block_table=b4.block_tables, out=out4),
         "norm_rope_prefill": lambda: pa.pa_qk_norm_rope_store(b3.qkv, nr_qw, nr_kw, 1e-6, nr_table, nr_pos,
                                                               b3.k_cache, b3.v_cache, b3.slot_mapping, 16,
                                                               q_out=nr_q),
@@ -466,21 +545,44 @@ def main():
         t = [ev[i][n][0].elapsed_time(ev[i][n][1]) * 1e3 for i in range(args.steps)]
         stats[name] = {"median": round(float(np.median(t)), 2), "min": round(float(np.min(t)), 2),
                        "max": round(float(np.max(t)), 2)}
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     peaks = measured_peaks(torch, dev)
     # after the timed steps: each launch alone with the caches flushed first (a 512 MiB write, untimed);
     # skipped in profiling runs, whose per-kernel statistics cover the timed steps only
     cold = None if args.step_only else cold_launches(torch, dev, kernels, calls)
 
+    def hbm_roofline(kernel: str, leg: str, nbytes: int, traffic=None, **extra):
+        gbs = nbytes / (ms[leg] * 1e-3) / 1e9
+        return {"bound": "hbm", "kernel": kernel, "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic, "bytes_per_launch": nbytes,
+                "avg_launch_us": round(ms[leg] * 1e3, 2), **extra}
+
+    def mfma_roofline(kernel: str, leg: str, flops: int):
+        tf = flops / (ms[leg] * 1e-3) / 1e12
+        return {"bound": "mfma", "kernel": kernel, "achieved": round(tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                "frac_of_measured_gemm": round(tf / peaks["bf16_gemm_TFLOPs"], 4), "flops_per_launch": flops,
+                "avg_launch_us": round(ms[leg] * 1e3, 2)}
+
     dbytes = decode_bytes(wl2)
     leg_bytes = dbytes["total"] + store_bytes(wl2, wl2.num_seqs)  # the decode plus the new tokens' store
     value = dbytes["kv"] / (ms["decode"] * 1e-3) / 1e9
-    achieved = leg_bytes / (ms["decode"] * 1e-3) / 1e9
     f3, f4 = prefill_flops(wl3), prefill_flops(wl4)
-    t3 = f3 / (ms["prefill"] * 1e-3) / 1e12
-    t4 = f4 / (ms["prefill_prefix"] * 1e-3) / 1e12
     nrb = norm_rope_bytes(wl3, wl3.num_tokens)
     smp_bytes = wl2.num_seqs * (SAMPLER_VOCAB * 4 + 4 + 4)
     sb = {"store_prefill": store_bytes(wl3, wl3.num_tokens), "store_prefix": store_bytes(wl4, wl4.num_tokens)}
+    workload = ("decode step of 256 seqs, context U{100..2048} (Hq 16, Hkv 8, D 128, 256-token blocks, "
+                "4096-block pool)")
+    if b5 is not None:
+        workload += (" + long-context decode step of 512 seqs, context log-uniform 256..32768 (Hq 32, Hkv 8, "
+                     "164,794-block pool)")
+    workload += (" + varlen causal prefill (%d seqs, %d tokens) + prefix-cached prefill (32 seqs, 1024 shared + "
+                 "%d new tokens)" % (wl3.num_seqs, wl3.num_tokens, wl4.num_tokens))
 
     result = {
         "metric": METRIC,
@@ -496,67 +598,52 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": "decode step of 256 seqs, context U{100..2048} (Hq 16, Hkv 8, D 128, 256-token blocks, "
-                        "4096-block pool) + varlen causal prefill (%d seqs, %d tokens) + prefix-cached prefill "
-                        "(32 seqs, 1024 shared + %d new tokens)" % (wl3.num_seqs, wl3.num_tokens, wl4.num_tokens),
+            "workload": workload,
+            "value_is": "KV-read GB/s of the 256-sequence decode leg (K and V bytes of every context token over "
+                        "the leg's event time)",
             "decode_kv_bytes": dbytes["kv"],
             "decode_split_waves": pa.pa_decode_split_waves(wl2.num_seqs, 16, 8, mk2, args.split_waves),
             "prefill_flops": f3,
             "prefix_prefill_flops": f4,
         },
-        "roofline": {"bound": "hbm", "kernel": "pa_store_decode (split kernel with the store fused + finalize)",
-                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
-                     "bytes_per_launch": leg_bytes, "avg_launch_us": round(ms["decode"] * 1e3, 2)},
-        "roofline_prefill": {"bound": "mfma", "kernel": "prefill_kernel (varlen, packed)", "achieved": round(t3, 1),
-                             "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                             "frac": round(t3 / MFMA_BF16_PEAK_TFLOPS, 4),
-                             "frac_of_measured_gemm": round(t3 / peaks["bf16_gemm_TFLOPs"], 4),
-                             "avg_launch_us": round(ms["prefill"] * 1e3, 2)},
-        "roofline_prefix_prefill": {"bound": "mfma", "kernel": "prefill_kernel (block table)",
-                                    "achieved": round(t4, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                                    "frac": round(t4 / MFMA_BF16_PEAK_TFLOPS, 4),
-                                    "frac_of_measured_gemm": round(t4 / peaks["bf16_gemm_TFLOPs"], 4),
-                                    "avg_launch_us": round(ms["prefill_prefix"] * 1e3, 2)},
-        "roofline_norm_rope_store": {"bound": "hbm", "kernel": "norm_rope_store_kernel (varlen prefill batch)",
-                                     "achieved": round(nrb / (ms["norm_rope_prefill"] * 1e-3) / 1e9, 1),
-                                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                     "frac": round(nrb / (ms["norm_rope_prefill"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                                     "bytes_per_launch": nrb,
-                                     "avg_launch_us": round(ms["norm_rope_prefill"] * 1e3, 2)},
-        "roofline_sampler": {"bound": "hbm", "kernel": "sample_partial + sample_final (256 x 151936 fp32 logits)",
-                             "achieved": round(smp_bytes / (ms["sample_decode"] * 1e-3) / 1e9, 1),
-                             "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                             "frac": round(smp_bytes / (ms["sample_decode"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                             "bytes_per_launch": smp_bytes, "avg_launch_us": round(ms["sample_decode"] * 1e3, 2)},
+        "pages_end_to_end_context": PAGES_END_TO_END,
+        "roofline": hbm_roofline("pa_store_decode (split kernel with the store fused + finalize)", "decode",
+                                 leg_bytes, measured_traffic("decode")),
+        "roofline_prefill": mfma_roofline("prefill_kernel (varlen, packed)", "prefill", f3),
+        "roofline_prefix_prefill": mfma_roofline("prefill_kernel (block table)", "prefill_prefix", f4),
+        "roofline_norm_rope_store": hbm_roofline("norm_rope_store_kernel (varlen prefill batch)",
+                                                 "norm_rope_prefill", nrb),
+        "roofline_sampler": hbm_roofline("sample_partial + sample_final (256 x 151936 fp32 logits)",
+                                         "sample_decode", smp_bytes),
+        "roofline_store": {k: hbm_roofline("store_tokens_kernel (%s batch)" % (
+                               "varlen" if k == "store_prefill" else "prefix"), k, sb[k],
+                               frac_of_measured_copy=round(sb[k] / (ms[k] * 1e-3) / 1e9 / peaks["copy_GBs"], 4))
+                           for k in sb},
         "kernels_us": {k: round(v * 1e3, 2) for k, v in ms.items()},
         "kernels_us_stats": stats,
         "kernels_us_cold": cold,
         "measured_peaks": peaks,
-        "store_GBs": {k: round(sb[k] / (ms[k] * 1e-3) / 1e9, 1) for k in sb},
-        "roofline_store": {k: {"bound": "hbm", "kernel": "store_tokens_kernel (%s batch)" % (
-                                   "varlen" if k == "store_prefill" else "prefix"),
-                               "achieved": round(sb[k] / (ms[k] * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
-                               "unit": "GB/s", "frac": round(sb[k] / (ms[k] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                               "frac_of_measured_copy": round(sb[k] / (ms[k] * 1e-3) / 1e9 / peaks["copy_GBs"], 4),
-                               "bytes_per_launch": sb[k], "avg_launch_us": round(ms[k] * 1e3, 2)} for k in sb},
     }
-    if args.copy_calibration:
-        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
+    if b5 is not None:
+        d5 = decode_bytes(wl5)
+        result["config"]["long_decode_kv_bytes"] = d5["kv"]
+        result["config"]["long_decode_split_waves"] = pa.pa_decode_split_waves(wl5.num_seqs, 32, 8,
+                                                                               wl5.max_context_len, args.split_waves)
+        result["roofline_long_decode"] = hbm_roofline(
+            "pa_store_decode (split kernel with the store fused + finalize), long-context batch", "long_decode",
+            d5["total"] + store_bytes(wl5, wl5.num_seqs), measured_traffic("long_decode"),
+            kv_GBs=round(d5["kv"] / (ms["long_decode"] * 1e-3) / 1e9, 1))
     if not args.step_only:
-        result["decode_separate_calls"] = separate_decode_leg(pa, torch, b2, wl2, scale, mk2, ws, out2, args)
-    if args.long_decode:
-        result["long_decode"] = long_decode(pa, torch, dev)
-    if not args.step_only and not args.long_decode:
+        result["decode_separate_calls"] = separate_decode_leg(pa, torch, b2, wl2, scale, mk2, ws, out2, args.steps,
+                                                              args.warmup, args.split_waves)
+        if b5 is not None:
+            result["long_decode_separate_calls"] = separate_decode_leg(
+                pa, torch, b5, wl5, scale, wl5.max_context_len, ws5, out5, args.steps, args.warmup, args.split_waves)
         result["host_block_manager"] = host_block_manager(wl2, wl4)
         result["decode_graph"] = decode_graph_latency(pa, torch, b2, wl2, scale)
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(b2, wl2)
-        result["cpu_baseline_prefill"] = cpu_baseline_prefill(b3, wl3)
-    print(json.dumps(result), flush=True)
+    if pool is not None:
+        result.update(cpu_baselines(pool, n_cores, b2, wl2, b3, wl3, b4, wl4, b5, wl5))
+    return result
 
 
 if __name__ == "__main__":

@@ -188,7 +188,7 @@ int pa_decode(void* out, const void* q, int64_t q_seq_stride, const void* k_cach
               size_t workspace_bytes, void* stream);
 
 /*
- * pa_store_decode — the decode step's store and pa_decode in one launch.
+ * pa_store_decode — the decode step's store and pa_decode in one call.
  *
  * Same result as pa_store_kvcache of each sequence's new token followed by
  * pa_decode (page "nano-vLLM 最小化vLLM重新实现", section 5 "注意力机制": the
@@ -199,9 +199,11 @@ int pa_decode(void* out, const void* q, int64_t q_seq_stride, const void* k_cach
  * block_tables[b, (L - 1) / block_size], and out is pa_decode's output over
  * positions 0 .. L - 1, the new token included. Sequences with L == 0 store
  * nothing and give zero rows. The new token's position comes from the block
- * table (no slot_mapping): the wave that reads the sequence's last chunk
- * writes the row, waits for the write and then reads it, so no other work
- * in the launch depends on it.
+ * table (no slot_mapping). Two kernels run: the split kernel takes position
+ * L - 1's K/V from k_new / v_new instead of the cache (in the one chunk
+ * that covers it), and the finalize kernel, which runs after it, writes the
+ * row into the cache, so nothing in the call reads the cache row before it
+ * is written.
  *
  * k_new, v_new  [num_seqs, num_kv_heads, head_dim] bf16, heads x dims
  *               contiguous, rows k_new_stride / v_new_stride elements apart
@@ -245,13 +247,16 @@ int pa_store_decode(void* out, const void* q, int64_t q_seq_stride, const void* 
  *               PA_ERR_UNSUPPORTED.
  * cu_seqlens_q, cu_seqlens_k  [num_seqs + 1] int32, non-decreasing from 0.
  * max_seqlen_q  upper bound of every nq (sizes the launch grid).
- * max_seqlen_k  upper bound of every nk; selects the key tile (32 keys up to
- *               1024, else 64). It only affects speed: results are correct
- *               for any value.
+ * max_seqlen_k  the longest key range the caller expects; selects the key
+ *               tile (32 keys up to 1024, else 64). Results do not depend on
+ *               it. With a block table, a value above max_blocks_per_seq *
+ *               block_size returns PA_ERR_INVALID_ARGUMENT (the table cannot
+ *               address that many keys).
  * block_table   optional [num_seqs, max_blocks_per_seq] int32; row i must
  *               name a block for every one of sequence i's keys
- *               (max_blocks_per_seq * block_size >= nk); entries past
- *               max_blocks_per_seq are never read.
+ *               (max_blocks_per_seq * block_size >= nk, a precondition the
+ *               device does not check); entries past max_blocks_per_seq are
+ *               never read.
  */
 int pa_prefill_varlen(void* out, const void* q, int64_t q_token_stride, const void* k, const void* v,
                       int64_t k_token_stride, int64_t v_token_stride, const int32_t* cu_seqlens_q,

@@ -29,8 +29,6 @@ Readings where the pages are silent (each is listed in the design doc):
 
 from __future__ import annotations
 
-import math
-
 import numpy as np
 
 
@@ -177,7 +175,3 @@ def prefill_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale: float, causal: bo
             out[q0:q1, h] = attention_rows(qi[:, h], keys[:, g], values[:, g], scale, last_key)
     return out
 
-
-def default_scale(head_dim: int) -> float:
-    """``1 / sqrt(head_dim)`` (page at bxzpzcl.cn/news/2159246, section 2.2.2)."""
-    return 1.0 / math.sqrt(head_dim)

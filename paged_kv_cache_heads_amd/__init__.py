@@ -46,16 +46,16 @@ def _ptr(t) -> int:
 _BF16, _I32, _F32, _U8 = torch.bfloat16, torch.int32, torch.float32, torch.uint8
 
 
-def _want(t, name: str, dtype, dim=None, contiguous=False, device=None, optional=False):
+def _want(t, name: str, dtype, dim=None, contiguous=False, optional=False) -> None:
     """Check a tensor argument before its address crosses the C ABI (which sees only pointers).
 
-    Raises TypeError for a non-tensor or a wrong dtype and ValueError for a wrong rank, a required
-    but missing contiguity, a tensor off the GPU or on another device than the call's. Returns
-    the tensor's device.
+    Raises TypeError for a non-tensor or a wrong dtype and ValueError for a wrong rank or a
+    required but missing contiguity. Shapes across arguments are checked next (_shape), and
+    the device last (_device), so every shape mismatch is reported even for host tensors.
     """
     if t is None:
         if optional:
-            return device
+            return
         raise TypeError(f"{name} is required")
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
@@ -65,11 +65,31 @@ def _want(t, name: str, dtype, dim=None, contiguous=False, device=None, optional
         raise ValueError(f"{name} must have {dim} dimensions, got shape {tuple(t.shape)}")
     if contiguous and not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
-    if t.device.type != "cuda":
-        raise ValueError(f"{name} must be on a GPU, got {t.device}")
-    if device is not None and t.device != device:
-        raise ValueError(f"{name} is on {t.device}, other arguments on {device}")
-    return t.device
+
+
+def _shape(t, name: str, want) -> None:
+    """ValueError unless t (if given) has shape `want`; None in `want` matches any extent."""
+    if t is None:
+        return
+    got = tuple(t.shape)
+    if len(got) != len(want) or any(w is not None and int(w) != g for g, w in zip(got, want)):
+        shown = tuple("*" if w is None else int(w) for w in want)
+        raise ValueError(f"{name} must have shape {shown}, got {got}")
+
+
+def _device(**tensors) -> torch.device:
+    """The one GPU all given tensors sit on; ValueError for a host tensor or a mix of devices."""
+    dev = None
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be on a GPU, got {t.device}")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, other arguments on {dev}")
+    return dev
 
 
 def _stream(stream, device) -> int:
@@ -100,16 +120,21 @@ def pa_version() -> int:
 
 def pa_store_kvcache(k, v, k_cache, v_cache, slot_mapping, stream=None) -> None:
     """Write k[t] / v[t] ([T, Hkv, D] bf16) into the caches ([NB, bs, Hkv, D]) at slot_mapping[t]."""
-    dev = _want(k_cache, "k_cache", _BF16, 4, True)
-    _want(v_cache, "v_cache", _BF16, 4, True, dev)
-    _want(k, "k", _BF16, 3, device=dev)
-    _want(v, "v", _BF16, 3, device=dev)
-    _want(slot_mapping, "slot_mapping", _I32, 1, True, dev)
-    lib = _lib.load()
+    _want(k_cache, "k_cache", _BF16, 4, True)
+    _want(v_cache, "v_cache", _BF16, 4, True)
+    _want(k, "k", _BF16, 3)
+    _want(v, "v", _BF16, 3)
+    _want(slot_mapping, "slot_mapping", _I32, 1, True)
     nb, bs, hkv, d = k_cache.shape
+    t = int(slot_mapping.shape[0])
+    _shape(v_cache, "v_cache", k_cache.shape)
+    _shape(k, "k", (t, hkv, d))
+    _shape(v, "v", (t, hkv, d))
+    dev = _device(k_cache=k_cache, v_cache=v_cache, k=k, v=v, slot_mapping=slot_mapping)
+    lib = _lib.load()
     _check("pa_store_kvcache", lib.pa_store_kvcache(
         _ptr(k), _rows(k, "k"), _ptr(v), _rows(v, "v"), _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping),
-        int(slot_mapping.shape[0]), hkv, d, nb, bs, _stream(stream, k_cache.device)))
+        t, hkv, d, nb, bs, _stream(stream, dev)))
 
 
 def pa_qk_norm_rope_store(qkv, q_norm_weight, k_norm_weight, eps: float, cos_sin, positions, k_cache, v_cache,
@@ -119,26 +144,37 @@ def pa_qk_norm_rope_store(qkv, q_norm_weight, k_norm_weight, eps: float, cos_sin
     cos_sin: [max_position, D] fp32 (cosines, then sines); positions, slot_mapping: [T] int32.
     Returns q_out [T, Hq, D] bf16 (allocated when not given; may be a view of qkv's q columns).
     """
-    dev = _want(qkv, "qkv", _BF16, 2)
+    _want(qkv, "qkv", _BF16, 2)
     for name, x in (("k_cache", k_cache), ("v_cache", v_cache)):
-        _want(x, name, _BF16, 4, True, dev)
+        _want(x, name, _BF16, 4, True)
     for name, x in (("q_norm_weight", q_norm_weight), ("k_norm_weight", k_norm_weight)):
-        _want(x, name, _BF16, 1, True, dev)
-    _want(cos_sin, "cos_sin", _F32, 2, True, dev)
-    _want(positions, "positions", _I32, 1, True, dev)
-    _want(slot_mapping, "slot_mapping", _I32, 1, True, dev)
-    _want(q_out, "q_out", _BF16, 3, device=dev, optional=True)
-    lib = _lib.load()
+        _want(x, name, _BF16, 1, True)
+    _want(cos_sin, "cos_sin", _F32, 2, True)
+    _want(positions, "positions", _I32, 1, True)
+    _want(slot_mapping, "slot_mapping", _I32, 1, True)
+    _want(q_out, "q_out", _BF16, 3, optional=True)
     nb, bs, hkv, d = k_cache.shape
-    t = int(qkv.shape[0])
-    if qkv.dim() != 2 or qkv.stride(1) != 1:
+    t, hq = int(qkv.shape[0]), int(num_q_heads)
+    _shape(v_cache, "v_cache", k_cache.shape)
+    _shape(qkv, "qkv", (t, (hq + 2 * hkv) * d))
+    _shape(q_norm_weight, "q_norm_weight", (d,))
+    _shape(k_norm_weight, "k_norm_weight", (d,))
+    _shape(cos_sin, "cos_sin", (None, d))
+    _shape(positions, "positions", (t,))
+    _shape(slot_mapping, "slot_mapping", (t,))
+    _shape(q_out, "q_out", (t, hq, d))
+    if qkv.stride(1) != 1:
         raise ValueError(f"qkv must be [T, (Hq + 2 Hkv) * D] with contiguous columns, got strides {qkv.stride()}")
+    dev = _device(qkv=qkv, k_cache=k_cache, v_cache=v_cache, q_norm_weight=q_norm_weight,
+                  k_norm_weight=k_norm_weight, cos_sin=cos_sin, positions=positions, slot_mapping=slot_mapping,
+                  q_out=q_out)
+    lib = _lib.load()
     if q_out is None:
-        q_out = torch.empty((t, num_q_heads, d), dtype=torch.bfloat16, device=qkv.device)
+        q_out = torch.empty((t, hq, d), dtype=torch.bfloat16, device=dev)
     _check("pa_qk_norm_rope_store", lib.pa_qk_norm_rope_store(
         _ptr(q_out), _rows(q_out, "q_out"), _ptr(qkv), qkv.stride(0), _ptr(q_norm_weight), _ptr(k_norm_weight),
         float(eps), _ptr(cos_sin), int(cos_sin.shape[0]), _ptr(positions), _ptr(k_cache), _ptr(v_cache),
-        _ptr(slot_mapping), t, int(num_q_heads), hkv, d, nb, bs, _stream(stream, qkv.device)))
+        _ptr(slot_mapping), t, hq, hkv, d, nb, bs, _stream(stream, dev)))
     return q_out
 
 
@@ -148,23 +184,26 @@ def pa_sample_workspace_size(num_rows: int, vocab_size: int) -> int:
 
 def pa_sample_gumbel(logits, temperatures, seed: int, offset: int, tokens=None, workspace=None, stream=None):
     """One token per row of logits [B, V] fp32 (temperatures [B] fp32): int32 [B]."""
-    dev = _want(logits, "logits", _F32, 2)
-    _want(temperatures, "temperatures", _F32, 1, True, dev)
-    _want(tokens, "tokens", _I32, 1, True, dev, optional=True)
-    _want(workspace, "workspace", _U8, 1, True, dev, optional=True)
-    lib = _lib.load()
+    _want(logits, "logits", _F32, 2)
+    _want(temperatures, "temperatures", _F32, 1, True)
+    _want(tokens, "tokens", _I32, 1, True, optional=True)
+    _want(workspace, "workspace", _U8, 1, True, optional=True)
     b, v = int(logits.shape[0]), int(logits.shape[1])
-    if logits.dim() != 2 or logits.stride(1) != 1:
+    _shape(temperatures, "temperatures", (b,))
+    _shape(tokens, "tokens", (b,))
+    if logits.stride(1) != 1:
         raise ValueError("logits must be [rows, vocab] with contiguous rows")
+    dev = _device(logits=logits, temperatures=temperatures, tokens=tokens, workspace=workspace)
+    lib = _lib.load()
     if tokens is None:
-        tokens = torch.empty(b, dtype=torch.int32, device=logits.device)
+        tokens = torch.empty(b, dtype=torch.int32, device=dev)
     need = lib.pa_sample_workspace_size(b, v)
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=logits.device)
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     _check("pa_sample_gumbel", lib.pa_sample_gumbel(
         _ptr(tokens), _ptr(logits), logits.stride(0), _ptr(temperatures), b, v, int(seed) & (2 ** 64 - 1),
         int(offset) & (2 ** 64 - 1), _ptr(workspace), workspace.numel() * workspace.element_size(),
-        _stream(stream, logits.device)))
+        _stream(stream, dev)))
     return tokens
 
 
@@ -179,15 +218,33 @@ def pa_decode_split_waves(num_seqs, num_q_heads, num_kv_heads, max_context_len, 
                                                  split_waves))
 
 
-def _decode_args(q, k_cache, v_cache, block_tables, context_lens, out, workspace):
-    dev = _want(q, "q", _BF16, 3)
-    _want(k_cache, "k_cache", _BF16, 4, True, dev)
-    _want(v_cache, "v_cache", _BF16, 4, True, dev)
-    _want(block_tables, "block_tables", _I32, 2, True, dev)
-    _want(context_lens, "context_lens", _I32, 1, True, dev)
-    _want(out, "out", _BF16, 3, True, dev, optional=True)
-    _want(workspace, "workspace", _U8, 1, True, dev, optional=True)
-    return dev
+def _decode_args(q, k_cache, v_cache, block_tables, context_lens, out, workspace, k_new=None, v_new=None,
+                 need_new=False, batch=None):
+    """Checks shared by the decode entry points: dtypes and ranks, then every shape against
+    q [B, Hq, D] and the cache [NB, bs, Hkv, D] (batch: the rows the buffers must hold, B by
+    default), then the device. Returns the device."""
+    _want(q, "q", _BF16, 3)
+    _want(k_cache, "k_cache", _BF16, 4, True)
+    _want(v_cache, "v_cache", _BF16, 4, True)
+    _want(block_tables, "block_tables", _I32, 2, True)
+    _want(context_lens, "context_lens", _I32, 1, True)
+    _want(out, "out", _BF16, 3, True, optional=True)
+    _want(workspace, "workspace", _U8, 1, True, optional=True)
+    _want(k_new, "k_new", _BF16, 3, optional=not need_new)
+    _want(v_new, "v_new", _BF16, 3, optional=not need_new)
+    b, hq, d = (int(x) for x in q.shape)
+    b = b if batch is None else int(batch)
+    _shape(q, "q", (b, hq, d))
+    _shape(v_cache, "v_cache", k_cache.shape)
+    _shape(k_cache, "k_cache", (None, None, None, d))
+    hkv = int(k_cache.shape[2])
+    _shape(block_tables, "block_tables", (b, None))
+    _shape(context_lens, "context_lens", (b,))
+    _shape(out, "out", (b, hq, d))
+    _shape(k_new, "k_new", (b, hkv, d))
+    _shape(v_new, "v_new", (b, hkv, d))
+    return _device(q=q, k_cache=k_cache, v_cache=v_cache, block_tables=block_tables, context_lens=context_lens,
+                   out=out, workspace=workspace, k_new=k_new, v_new=v_new)
 
 
 def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, max_context_len: int, out=None,
@@ -197,47 +254,47 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, max
     workspace: a uint8 device tensor of at least pa_decode_workspace_size(...)
     bytes; allocated here when not given.
     """
-    _decode_args(q, k_cache, v_cache, block_tables, context_lens, out, workspace)
+    dev = _decode_args(q, k_cache, v_cache, block_tables, context_lens, out, workspace)
     lib = _lib.load()
     b, hq, d = q.shape
     nb, bs, hkv, _ = k_cache.shape
     if out is None:
-        out = torch.empty((b, hq, d), dtype=torch.bfloat16, device=q.device)
+        out = torch.empty((b, hq, d), dtype=torch.bfloat16, device=dev)
     need = lib.pa_decode_workspace_size(b, hq, hkv, d, max_context_len, split_waves)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("pa_decode", lib.pa_decode(
         _ptr(out), _ptr(q), _rows(q, "q"), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
         int(block_tables.shape[1]), _ptr(context_lens), b, hq, hkv, d, bs, int(max_context_len), float(scale),
-        int(split_waves), _ptr(workspace), ws_bytes, _stream(stream, q.device)))
+        int(split_waves), _ptr(workspace), ws_bytes, _stream(stream, dev)))
     return out
 
 
 def pa_store_decode(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale: float,
                     max_context_len: int, out=None, workspace=None, split_waves: int = 0, stream=None):
     """Store each sequence's new token at position L - 1 (through its block table), then paged decode:
-    q [B, Hq, D], k_new / v_new [B, Hkv, D] bf16 -> out [B, Hq, D] bf16, in one launch.
+    q [B, Hq, D], k_new / v_new [B, Hkv, D] bf16 -> out [B, Hq, D] bf16.
 
+    Two kernels: the split kernel reads the new token's K/V from k_new / v_new, and the finalize
+    kernel, which runs after it, writes them into the cache at position L - 1.
     workspace: as for pa_decode (allocated here when not given).
     """
-    dev = _decode_args(q, k_cache, v_cache, block_tables, context_lens, out, workspace)
-    _want(k_new, "k_new", _BF16, 3, device=dev)
-    _want(v_new, "v_new", _BF16, 3, device=dev)
+    dev = _decode_args(q, k_cache, v_cache, block_tables, context_lens, out, workspace, k_new, v_new, True)
     lib = _lib.load()
     b, hq, d = q.shape
     nb, bs, hkv, _ = k_cache.shape
     if out is None:
-        out = torch.empty((b, hq, d), dtype=torch.bfloat16, device=q.device)
+        out = torch.empty((b, hq, d), dtype=torch.bfloat16, device=dev)
     need = lib.pa_decode_workspace_size(b, hq, hkv, d, max_context_len, split_waves)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("pa_store_decode", lib.pa_store_decode(
         _ptr(out), _ptr(q), _rows(q, "q"), _ptr(k_new), _rows(k_new, "k_new"), _ptr(v_new), _rows(v_new, "v_new"),
         _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), int(block_tables.shape[1]), _ptr(context_lens), b, hq,
         hkv, d, bs, int(max_context_len), float(scale), int(split_waves), _ptr(workspace), ws_bytes,
-        _stream(stream, q.device)))
+        _stream(stream, dev)))
     return out
 
 
@@ -248,29 +305,38 @@ def pa_prefill_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, ma
     Without block_table, k / v are packed [Tk, Hkv, D] (row strides may exceed
     Hkv * D); with it, k / v are the caches [NB, bs, Hkv, D].
     """
-    dev = _want(q, "q", _BF16, 3)
+    _want(q, "q", _BF16, 3)
     kdim = 3 if block_table is None else 4
-    _want(k, "k", _BF16, kdim, block_table is not None, dev)
-    _want(v, "v", _BF16, kdim, block_table is not None, dev)
-    _want(cu_seqlens_q, "cu_seqlens_q", _I32, 1, True, dev)
-    _want(cu_seqlens_k, "cu_seqlens_k", _I32, 1, True, dev)
-    _want(block_table, "block_table", _I32, 2, True, dev, optional=True)
-    _want(out, "out", _BF16, 3, True, dev, optional=True)
+    _want(k, "k", _BF16, kdim, block_table is not None)
+    _want(v, "v", _BF16, kdim, block_table is not None)
+    _want(cu_seqlens_q, "cu_seqlens_q", _I32, 1, True)
+    _want(cu_seqlens_k, "cu_seqlens_k", _I32, 1, True)
+    _want(block_table, "block_table", _I32, 2, True, optional=True)
+    _want(out, "out", _BF16, 3, True, optional=True)
+    tq, hq, d = (int(x) for x in q.shape)
+    num_seqs = int(cu_seqlens_q.shape[0]) - 1
+    if num_seqs < 0:
+        raise ValueError("cu_seqlens_q must hold num_seqs + 1 >= 1 offsets")
+    _shape(cu_seqlens_k, "cu_seqlens_k", cu_seqlens_q.shape)
+    _shape(out, "out", q.shape)
+    _shape(v, "v", k.shape)
+    _shape(k, "k", (None,) * (kdim - 1) + (d,))
+    _shape(block_table, "block_table", (num_seqs, None))
+    dev = _device(q=q, k=k, v=v, cu_seqlens_q=cu_seqlens_q, cu_seqlens_k=cu_seqlens_k, block_table=block_table,
+                  out=out)
     lib = _lib.load()
-    tq, hq, d = q.shape
     if out is None:
-        out = torch.empty((tq, hq, d), dtype=torch.bfloat16, device=q.device)
+        out = torch.empty((tq, hq, d), dtype=torch.bfloat16, device=dev)
     if block_table is None:
-        hkv = k.shape[1]
+        hkv = int(k.shape[1])
         ks, vs, width, bs = _rows(k, "k"), _rows(v, "v"), 0, 0
     else:
-        _, bs, hkv, _ = k.shape
+        _, bs, hkv, _ = (int(x) for x in k.shape)
         ks, vs, width = hkv * d, hkv * d, int(block_table.shape[1])
     _check("pa_prefill_varlen", lib.pa_prefill_varlen(
         _ptr(out), _ptr(q), _rows(q, "q"), _ptr(k), _ptr(v), ks, vs, _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
-        int(cu_seqlens_q.shape[0]) - 1, int(max_seqlen_q), int(max_seqlen_k), hq, hkv, d, float(scale),
-        1 if causal else 0,
-        _ptr(block_table), width, bs, _stream(stream, q.device)))
+        num_seqs, int(max_seqlen_q), int(max_seqlen_k), hq, hkv, d, float(scale), 1 if causal else 0,
+        _ptr(block_table), width, bs, _stream(stream, dev)))
     return out
 
 
@@ -288,11 +354,21 @@ class DecodeGraphs:
                  v_cache, scale: float, max_context_len: int, batch_sizes, split_waves: int = 0, stream=None):
         import ctypes
 
-        dev = _decode_args(q, k_cache, v_cache, block_tables, context_lens, out, workspace)
-        _want(workspace, "workspace", _U8, 1, True, dev)
-        _want(k_new, "k_new", _BF16, 3, device=dev)
-        _want(v_new, "v_new", _BF16, 3, device=dev)
-        _want(slot_mapping, "slot_mapping", _I32, 1, True, dev)
+        if workspace is None:
+            raise TypeError("workspace is required")
+        if out is None:
+            raise TypeError("out is required")
+        _want(q, "q", _BF16, 3)
+        _want(slot_mapping, "slot_mapping", _I32, 1, True)
+        sizes_list = [int(b) for b in batch_sizes]
+        if not sizes_list or min(sizes_list) < 1:
+            raise ValueError(f"batch_sizes must be positive, got {sizes_list}")
+        rows = int(q.shape[0])
+        if max(sizes_list) > rows:
+            raise ValueError(f"the step buffers hold {rows} rows, fewer than the largest batch size {max(sizes_list)}")
+        _shape(slot_mapping, "slot_mapping", (rows,))
+        dev = _decode_args(q, k_cache, v_cache, block_tables, context_lens, out, workspace, k_new, v_new, True)
+        _device(q=q, slot_mapping=slot_mapping)
         lib = _lib.load()
         self._lib = lib
         nb, bs, hkv, d = k_cache.shape

@@ -380,6 +380,11 @@ int pa_prefill_varlen(void* out, const void* q, int64_t q_token_stride, const vo
     if (max_blocks_per_seq <= 0)
       return fail(PA_ERR_INVALID_ARGUMENT, "max_blocks_per_seq %d must be positive with a block table",
                   max_blocks_per_seq);
+    // a table row names at most max_blocks_per_seq blocks: longer key ranges cannot be addressed
+    if ((int64_t)max_blocks_per_seq * block_size < max_seqlen_k)
+      return fail(PA_ERR_INVALID_ARGUMENT,
+                  "max_seqlen_k %d exceeds what a block table row covers (%d blocks of %d tokens)", max_seqlen_k,
+                  max_blocks_per_seq, block_size);
   } else {
     if (k_token_stride < kv_row || v_token_stride < kv_row)
       return fail(PA_ERR_INVALID_ARGUMENT, "k/v token strides (%lld, %lld) are below a row (%lld)",

@@ -168,6 +168,8 @@ def test_prefill_validation(lib):
     assert prefill(lib, q=A + 6) == ALIGN
     assert prefill(lib, bt=A, W=0, bs=256) == INVAL
     assert prefill(lib, bt=A, W=6, bs=96) == UNSUP
+    # a table of 3 blocks of 256 tokens cannot address 1024 keys
+    assert prefill(lib, bt=A, W=3, bs=256, maxk=1024) == INVAL
     assert prefill(lib, scale=float("inf")) == INVAL
     assert prefill(lib, S=0, out=None, q=None, k=None, v=None, cq=None, ck=None) == PA_OK
 

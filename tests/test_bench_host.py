@@ -56,9 +56,33 @@ def test_norm_rope_bytes():
     assert bench.norm_rope_bytes(wl, 3) == 3 * per_token + 2 * 128 * 2
 
 
-def test_cpu_baseline_prefill_reports_the_oracle():
-    wl = configs.prefill_workload("cpu", [20, 7], 0, 16, 8, 16, seed=2)
-    batch = tensors.materialize(wl, torch.device("cpu"))
-    r = bench.cpu_baseline_prefill(batch, wl, budget_s=5.0)
-    assert r["kind"] == "oracle" and r["unit"] == "TFLOP/s" and r["cores"] == 1
-    assert r["value"] > 0 and "2 of 2 sequences" in r["sample"]
+def test_balanced_shares():
+    shares = bench.balanced_shares([5, 1, 1, 1, 1, 1, 4], 3)
+    assert sorted(i for g in shares for i in g) == list(range(7))
+    loads = sorted(sum([5, 1, 1, 1, 1, 1, 4][i] for i in g) for g in shares)
+    assert loads == [4, 5, 5]
+    assert bench.balanced_shares([3], 4) == [[0]]
+
+
+def test_oracle_baselines_on_a_worker_pool():
+    # the unmodified oracle over shares of each batch, in spawned worker processes
+    pool = bench.start_oracle_pool(2)
+    try:
+        cpu = torch.device("cpu")
+        wl = configs.prefill_workload("cpu", [20, 7, 13], 0, 16, 8, 16, seed=2)
+        r = bench.run_oracle_baseline(pool, *bench.prefill_tasks(tensors.materialize(wl, cpu), wl, 2, paged=False),
+                                      "TFLOP/s", "packed")
+        assert r["kind"] == "oracle" and r["unit"] == "TFLOP/s" and r["cores"] == 2 and r["value"] > 0
+        assert r["oracle_s_slowest_share"] <= r["oracle_s_all_shares"]
+        wl = configs.prefill_workload("cpu-prefix", [9, 30], 64, 16, 8, 16, seed=3, block_size=64)
+        tasks, work = bench.prefill_tasks(tensors.materialize(wl, cpu), wl, 2, paged=True)
+        assert sum(work) == bench.prefill_flops(wl)
+        assert bench.run_oracle_baseline(pool, tasks, work, "TFLOP/s", "paged")["value"] > 0
+        wl = configs.decode_workload("cpu-decode", [5, 300, 40, 1], 16, 8, 8, seed=4)
+        tasks, work = bench.decode_tasks(tensors.materialize(wl, cpu), wl, [0, 1, 3], 2)
+        assert sum(work) == (5 + 300 + 1) * 8 * 128 * 4
+        r = bench.run_oracle_baseline(pool, tasks, work, "GB/s", "decode")
+        assert r["unit"] == "GB/s" and r["cores"] == 2 and r["value"] > 0
+    finally:
+        pool.terminate()
+        pool.join()

@@ -30,7 +30,7 @@ def _run(wl, dev, seqs=None, split_waves=0, extra_check=None, scale=None):
     torch.cuda.synchronize()
     host.store(k_new, v_new, slots, wl.block_size)
     ref = oracle.decode(q[seqs], host.k, host.v, host.tables, wl.context_lens[seqs], scale)
-    stats = assert_attention_close(out[seqs], ref, wl.name)
+    stats = assert_attention_close(out[seqs], ref, f"pa_decode {wl.name}")
     if extra_check:
         extra_check(batch, out)
     return stats

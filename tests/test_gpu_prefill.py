@@ -15,6 +15,16 @@ from workloads import configs, tensors
 pytestmark = pytest.mark.gpu
 
 
+def _cover(table, max_k: int, block_size: int):
+    """The block table padded with never-read -1 columns until a row covers max_k keys (the library
+    rejects a max_seqlen_k its table cannot address)."""
+    need = -(-max_k // block_size) - table.shape[1]
+    if need <= 0:
+        return table
+    pad = torch.full((table.shape[0], need), -1, dtype=table.dtype, device=table.device)
+    return torch.cat([table, pad], dim=1).contiguous()
+
+
 def _packed(wl, dev, causal=True, check_table_path=True, max_k=None, scale=None):
     """Prefill over packed q/k/v; the same keys read back through the cache must give identical bits.
 
@@ -30,11 +40,12 @@ def _packed(wl, dev, causal=True, check_table_path=True, max_k=None, scale=None)
     out_t = None
     if check_table_path:
         out_t = pa.pa_prefill_varlen(batch.q, batch.k_cache, batch.v_cache, batch.cu_seqlens_q, batch.cu_seqlens_k,
-                                     wl.max_seqlen_q, mk, scale, causal=causal, block_table=batch.block_tables)
+                                     wl.max_seqlen_q, mk, scale, causal=causal,
+                                     block_table=_cover(batch.block_tables, mk, wl.block_size))
     torch.cuda.synchronize()
     ref = oracle.prefill_varlen(tensors.to_u16(batch.q), tensors.to_u16(batch.k_new), tensors.to_u16(batch.v_new),
                                 wl.cu_seqlens_q, wl.cu_seqlens_k, scale, causal=causal)
-    stats = assert_attention_close(out, ref, wl.name)
+    stats = assert_attention_close(out, ref, f"pa_prefill_varlen packed {wl.name}")
     if out_t is not None:
         assert torch.equal(out.view(torch.int16), out_t.view(torch.int16)), "table path differs from packed path"
     return stats
@@ -50,12 +61,13 @@ def _table(wl, dev, causal=True, max_k=None):
     slots = batch.slot_mapping.cpu().numpy()
     pa.pa_store_kvcache(batch.k_new, batch.v_new, batch.k_cache, batch.v_cache, batch.slot_mapping)
     out = pa.pa_prefill_varlen(batch.q, batch.k_cache, batch.v_cache, batch.cu_seqlens_q, batch.cu_seqlens_k,
-                               wl.max_seqlen_q, mk, scale, causal=causal, block_table=batch.block_tables)
+                               wl.max_seqlen_q, mk, scale, causal=causal,
+                               block_table=_cover(batch.block_tables, mk, wl.block_size))
     torch.cuda.synchronize()
     host.store(k_new, v_new, slots, wl.block_size)
     ref = oracle.prefill_varlen(tensors.to_u16(batch.q), host.k, host.v, wl.cu_seqlens_q, wl.cu_seqlens_k, scale,
                                 causal=causal, block_table=host.tables)
-    return assert_attention_close(out, ref, wl.name)
+    return assert_attention_close(out, ref, f"pa_prefill_varlen table {wl.name}")
 
 
 @pytest.mark.parametrize("seed,max_k", [(3, None), (101, None), (3, 4096)])

@@ -43,7 +43,7 @@ def _run(wl, dev, split_waves=0, oracle_seqs=None):
     host.store(tensors.to_u16(batch.k_new), tensors.to_u16(batch.v_new), batch.slot_mapping.cpu().numpy(),
                wl.block_size)
     ref = oracle.decode(tensors.to_u16(batch.q)[seqs], host.k, host.v, host.tables, wl.context_lens[seqs], scale)
-    assert_attention_close(out[seqs], ref, wl.name)
+    assert_attention_close(out[seqs], ref, f"pa_store_decode {wl.name}")
 
 
 def test_store_decode_config1(dev):
