@@ -219,6 +219,36 @@ int pa_store_decode(void* out, const void* q, int64_t q_seq_stride, const void* 
                     size_t workspace_bytes, void* stream);
 
 /*
+ * pa_store_decode_noalloc — pa_store_decode without a caller workspace.
+ *
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * arguments, checks, kernels and results as pa_store_decode (bit for bit),
+ * with the workspace taken from a static device array inside the library
+ * (16.25 MiB per GPU, held until the process ends; its address is looked up
+ * once per device on the first call there). Nothing is allocated: no
+ * hipMalloc, no hipFree.
+ *
+ * Limit: the split must fit the static scratch, i.e. split_waves (or the
+ * library's default of 2048) times 2 slots times G query heads per kv head
+ * times 520 bytes at most 17,039,360 bytes; the default split fits every
+ * supported group. Larger splits return PA_ERR_WORKSPACE_TOO_SMALL and launch
+ * nothing.
+ *
+ * Every call on one GPU shares that GPU's scratch, and nothing in it has to
+ * start at zero (each call's finalize pass reads only what its split kernel
+ * wrote). Calls that overlap on one GPU (concurrent streams, or threads)
+ * race on it and give undefined results; calls ordered on one stream are
+ * safe.
+ */
+int pa_store_decode_noalloc(void* out, const void* q, int64_t q_seq_stride, const void* k_new, int64_t k_new_stride,
+                            const void* v_new, int64_t v_new_stride, void* k_cache, void* v_cache,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                            int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t block_size, int32_t max_context_len, float scale, int32_t split_waves,
+                            void* stream);
+
+/*
  * pa_prefill_varlen — attention over packed variable-length sequences.
  *
  * Page "nano-vLLM 最小化vLLM重新实现", section 5 "注意力机制": prefill over

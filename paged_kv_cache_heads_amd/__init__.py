@@ -18,7 +18,7 @@ from ._lib import LibraryMissing  # noqa: F401
 __all__ = [
     "PAError", "LibraryMissing", "pa_store_kvcache", "pa_qk_norm_rope_store", "pa_decode", "pa_store_decode",
     "pa_decode_workspace_size", "pa_decode_split_waves", "pa_prefill_varlen", "pa_status_string", "pa_last_error", "pa_version",
-    "library_path", "DecodeGraphs", "pa_sample_gumbel", "pa_sample_workspace_size",
+    "library_path", "DecodeGraphs", "pa_sample_gumbel", "pa_sample_workspace_size", "pa_store_decode_noalloc",
 ]
 
 
@@ -295,6 +295,23 @@ def pa_store_decode(q, k_new, v_new, k_cache, v_cache, block_tables, context_len
         _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), int(block_tables.shape[1]), _ptr(context_lens), b, hq,
         hkv, d, bs, int(max_context_len), float(scale), int(split_waves), _ptr(workspace), ws_bytes,
         _stream(stream, dev)))
+    return out
+
+
+def pa_store_decode_noalloc(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale: float,
+                            max_context_len: int, out, split_waves: int = 0, stream=None):
+    """pa_store_decode with the library's static scratch as the workspace: allocates nothing, so
+    `out` ([B, Hq, D] bf16) is required. Calls that overlap on one GPU race on the scratch."""
+    if out is None:
+        raise TypeError("out is required (this entry point allocates nothing)")
+    dev = _decode_args(q, k_cache, v_cache, block_tables, context_lens, out, None, k_new, v_new, True)
+    lib = _lib.load()
+    b, hq, d = q.shape
+    nb, bs, hkv, _ = k_cache.shape
+    _check("pa_store_decode_noalloc", lib.pa_store_decode_noalloc(
+        _ptr(out), _ptr(q), _rows(q, "q"), _ptr(k_new), _rows(k_new, "k_new"), _ptr(v_new), _rows(v_new, "v_new"),
+        _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), int(block_tables.shape[1]), _ptr(context_lens), b, hq,
+        hkv, d, bs, int(max_context_len), float(scale), int(split_waves), _stream(stream, dev)))
     return out
 
 

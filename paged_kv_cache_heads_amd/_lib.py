@@ -36,6 +36,8 @@ SIGNATURES = {
                                  _f32, _i32, _vp, _sz, _vp]),
     "pa_store_decode": (ctypes.c_int, [_vp, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _i32p, _i32, _i32p, _i32,
                                        _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp]),
+    "pa_store_decode_noalloc": (ctypes.c_int, [_vp, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _i32p, _i32, _i32p,
+                                               _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp]),
     "pa_prefill_varlen": (ctypes.c_int, [_vp, _vp, _i64, _vp, _vp, _i64, _i64, _i32p, _i32p, _i32, _i32, _i32, _i32,
                                          _i32, _i32, _f32, _i32, _i32p, _i32, _i32, _vp]),
     "pa_sample_workspace_size": (_sz, [_i32, _i32]),

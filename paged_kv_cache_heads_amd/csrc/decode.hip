@@ -40,10 +40,43 @@
 //   M = max m_i, o = sum 2^(m_i - M) o_i / sum 2^(m_i - M) l_i.
 #include <math.h>
 
+#include <mutex>
+
+#include "../../include/pa.h"
 #include "common.h"
 #include "launch.h"
 
 namespace pa {
+
+// Decode scratch for callers that cannot allocate (pa_store_decode_noalloc):
+// room for the fp32 partials of the default split (2048 waves x 2 slots) at the
+// largest group (8 query heads per kv head), 128 output values + (max, sum)
+// per slot and head. Nothing in it has to start at zero: the finalize pass
+// reads only the pieces this call's split kernel wrote. Each GPU the library
+// runs on holds its own copy until the process ends.
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+int decode_scratch(void** ptr) {
+  // The array's name is a host-side stand-in; its device address is looked up
+  // once per device, with that device current, and kept.
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(PA_ERR_UNSUPPORTED, "device %d is beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(PA_ERR_HIP, "hipGetSymbolAddress of the decode scratch: %s", hipGetErrorString(e));
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return PA_OK;
+}
 
 constexpr int kD = 128;
 // Sum of TPL values (tokens i*8 + r, i < TPL) over the 8 lanes of group r.

@@ -118,6 +118,11 @@ hipError_t launch_pad_decode_rows(int32_t* slot_mapping, int32_t* context_lens, 
                                   hipStream_t stream);
 // Tokens per decode work chunk for a GQA group size.
 int decode_chunk_tokens(int group);
+// The library's static decode scratch: 2048 waves x 2 slots x 8 heads x
+// (128 + 2) fp32 values. decode_scratch() gives its device address on the
+// current device (looked up once per device); PA_OK or a pa_status.
+constexpr size_t kDecodeScratchBytes = (size_t)2048 * 2 * 8 * (128 + 2) * sizeof(float);
+int decode_scratch(void** ptr);
 hipError_t launch_prefill(const PrefillArgs& a, int group, hipStream_t stream);
 
 // Query positions covered by one prefill workgroup for a GQA group size.

@@ -273,7 +273,7 @@ static int decode_impl(void* out, const void* q, int64_t q_seq_stride, const voi
                        const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
                        int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                        int32_t block_size, int32_t max_context_len, float scale, int32_t split_waves, void* workspace,
-                       size_t workspace_bytes, void* stream) {
+                       size_t workspace_bytes, void* stream, bool static_scratch = false) {
   if (num_seqs < 0) return fail(PA_ERR_INVALID_ARGUMENT, "num_seqs %d is negative", num_seqs);
   if (num_seqs > 65535) return fail(PA_ERR_UNSUPPORTED, "num_seqs %d exceeds 65535", num_seqs);
   int st = check_heads(num_q_heads, num_kv_heads, head_dim);
@@ -306,6 +306,16 @@ static int decode_impl(void* out, const void* q, int64_t q_seq_stride, const voi
   }
   DecodeGeometry g;
   decode_geometry(num_seqs, num_q_heads, num_kv_heads, max_context_len, split_waves, &g);
+  if (static_scratch) {
+    // pa_store_decode_noalloc: the library's static scratch is the workspace
+    if (g.ws_bytes > pa::kDecodeScratchBytes)
+      return fail(PA_ERR_WORKSPACE_TOO_SMALL,
+                  "this split needs %zu bytes of decode scratch; the static scratch holds %zu (at most 2048 "
+                  "waves x 8 query heads per kv head)", g.ws_bytes, pa::kDecodeScratchBytes);
+    const int sst = pa::decode_scratch(&workspace);
+    if (sst) return sst;
+    workspace_bytes = pa::kDecodeScratchBytes;
+  }
   if (!workspace) return fail(PA_ERR_NULL_POINTER, "workspace of %zu bytes is required", g.ws_bytes);
   if (workspace_bytes < g.ws_bytes)
     return fail(PA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < required %zu", workspace_bytes, g.ws_bytes);
@@ -357,6 +367,18 @@ int pa_store_decode(void* out, const void* q, int64_t q_seq_stride, const void* 
   return decode_impl(out, q, q_seq_stride, k_new, k_new_stride, v_new, v_new_stride, k_cache, v_cache, block_tables,
                      max_blocks_per_seq, context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                      max_context_len, scale, split_waves, workspace, workspace_bytes, stream);
+}
+
+int pa_store_decode_noalloc(void* out, const void* q, int64_t q_seq_stride, const void* k_new, int64_t k_new_stride,
+                            const void* v_new, int64_t v_new_stride, void* k_cache, void* v_cache,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                            int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t block_size, int32_t max_context_len, float scale, int32_t split_waves,
+                            void* stream) {
+  if (num_seqs > 0 && (!k_new || !v_new)) return fail(PA_ERR_NULL_POINTER, "k_new and v_new are required");
+  return decode_impl(out, q, q_seq_stride, k_new, k_new_stride, v_new, v_new_stride, k_cache, v_cache, block_tables,
+                     max_blocks_per_seq, context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                     max_context_len, scale, split_waves, nullptr, 0, stream, /*static_scratch=*/true);
 }
 
 int pa_prefill_varlen(void* out, const void* q, int64_t q_token_stride, const void* k, const void* v,

@@ -43,7 +43,7 @@ def test_header_declares_entry_points():
     names = declared_functions()
     for n in ["pa_store_kvcache", "pa_qk_norm_rope_store", "pa_decode", "pa_decode_workspace_size", "pa_prefill_varlen",
               "pa_status_string", "pa_last_error", "pa_bm_create", "pa_bm_allocate", "pa_bm_append_batch",
-              "pa_bm_prefill_metadata", "pa_xxh64"]:
+              "pa_bm_prefill_metadata", "pa_xxh64", "pa_store_decode_noalloc"]:
         assert n in names
 
 
@@ -130,6 +130,28 @@ def test_store_decode_validation(lib):
     assert store_decode(lib, W=7) == INVAL               # the decode checks apply too
     assert store_decode(lib, ws=None) == NULLP
     assert store_decode(lib, B=0, out=None, q=None, kn=None, vn=None, kc=None, vc=None, bt=None, cl=None) == PA_OK
+
+
+def store_decode_noalloc(lib, **kw):
+    a = dict(out=A, q=A, qs=2048, kn=A, kns=1024, vn=A, vns=1024, kc=A, vc=A, bt=A, W=8, cl=A, B=4, hq=16, hkv=8,
+             d=128, bs=256, maxL=2048, scale=0.088, part=0, stream=None)
+    a.update(kw)
+    return lib.pa_store_decode_noalloc(a["out"], a["q"], a["qs"], a["kn"], a["kns"], a["vn"], a["vns"], a["kc"],
+                                       a["vc"], a["bt"], a["W"], a["cl"], a["B"], a["hq"], a["hkv"], a["d"], a["bs"],
+                                       a["maxL"], a["scale"], a["part"], a["stream"])
+
+
+def test_store_decode_noalloc_validation(lib):
+    # the pa_store_decode checks, before the static scratch is looked up
+    assert store_decode_noalloc(lib, kn=None) == NULLP
+    assert store_decode_noalloc(lib, kns=512) == INVAL
+    assert store_decode_noalloc(lib, W=7) == INVAL
+    assert store_decode_noalloc(lib, d=64) == UNSUP
+    assert store_decode_noalloc(lib, B=0, out=None, q=None, kn=None, vn=None, kc=None, vc=None, bt=None,
+                                cl=None) == PA_OK
+    # a split larger than the static scratch (16.25 MiB) is refused with a clear message
+    assert store_decode_noalloc(lib, hq=64, hkv=8, qs=8192, part=2049, B=512, maxL=32768, W=128) == WS
+    assert "static scratch" in pa.pa_last_error()
 
 
 def test_decode_workspace_size(lib):
