@@ -217,43 +217,52 @@ def host_block_manager(wl2, wl4, reps=20):
 
 
 def decode_graph_latency(pa, torch, b2, wl2, scale, batches=(1, 16, 256), iters=200):
-    """Wall-clock time per decode step (store + decode), eager through the binding vs one
-    graph launch, for the first `batch` sequences of the decode batch (back to back on one
-    stream, synchronised once per measurement)."""
+    """Wall-clock time per decode step, eager pa_store_decode through the binding vs one graph launch
+    (inputs, including the graph's live count, written before the timed launches), for the first
+    `batch` sequences of the decode batch: back to back on one stream (synchronised once per
+    measurement), and isolated (each step launched and waited for)."""
     dev = b2.q.device
     sizes = [1, 2, 4, 8, 16, 32, 64, 128, 256]
     maxb = sizes[-1]
     w = int(b2.block_tables.shape[1])
     max_len = w * wl2.block_size
     q_s, k_s, v_s = b2.q.clone(), b2.k_new.contiguous(), b2.v_new.contiguous()
-    slot_s, bt_s, cl_s = b2.slot_mapping.clone(), b2.block_tables.clone(), b2.context_lens.clone()
+    bt_s, cl_s = b2.block_tables.clone(), b2.context_lens.clone()
     out_s = torch.empty_like(q_s)
     ws = torch.empty(pa.pa_decode_workspace_size(maxb, 16, 8, 128, max_len), dtype=torch.uint8, device=dev)
     stream = torch.cuda.Stream()
-    res = {"batch": list(batches), "eager_step_us": [], "graph_step_us": [], "captured_sizes": sizes}
+    res = {"batch": list(batches), "eager_step_us": [], "graph_step_us": [], "eager_isolated_step_us": [],
+           "graph_isolated_step_us": [], "captured_sizes": sizes}
     with torch.cuda.stream(stream):
-        graphs = pa.DecodeGraphs(q_s, k_s, v_s, slot_s, bt_s, cl_s, out_s, ws, b2.k_cache, b2.v_cache, scale,
-                                 max_len, sizes)
+        graphs = pa.DecodeGraphs(q_s, k_s, v_s, bt_s, cl_s, out_s, ws, b2.k_cache, b2.v_cache, scale, max_len,
+                                 sizes)
         for batch in batches:
             qs, ks, vs = q_s[:batch], k_s[:batch], v_s[:batch]
-            sl, bt, cl, o = slot_s[:batch], bt_s[:batch], cl_s[:batch], out_s[:batch]
+            bt, cl, o = bt_s[:batch], cl_s[:batch], out_s[:batch]
 
             def eager():
-                pa.pa_store_kvcache(ks, vs, b2.k_cache, b2.v_cache, sl)
-                pa.pa_decode(qs, b2.k_cache, b2.v_cache, bt, cl, scale, max_len, out=o, workspace=ws)
+                pa.pa_store_decode(qs, ks, vs, b2.k_cache, b2.v_cache, bt, cl, scale, max_len, out=o, workspace=ws)
 
-            for fn, key in ((eager, "eager_step_us"), (lambda: graphs.launch(batch), "graph_step_us")):
+            graphs.live_batch.fill_(batch)
+            for fn, key in ((eager, "eager"), (lambda: graphs.launch(batch, live_written=True), "graph")):
                 for _ in range(10):
                     fn()
                 stream.synchronize()
+                # back to back: the GPU's time per step once launches queue ahead of it
                 t0 = time.perf_counter()
                 for _ in range(iters):
                     fn()
                 stream.synchronize()
-                res[key].append(round((time.perf_counter() - t0) / iters * 1e6, 1))
-            # the graph padded rows batch .. padded - 1 of these buffers: restore them
-            slot_s.copy_(b2.slot_mapping)
-            cl_s.copy_(b2.context_lens)
+                res[key + "_step_us"].append(round((time.perf_counter() - t0) / iters * 1e6, 1))
+                # isolated: launch, then wait for the step (the per-token latency a sampler waiting on
+                # each step sees, launch cost included); median over the iterations
+                lat = []
+                for _ in range(iters):
+                    t0 = time.perf_counter()
+                    fn()
+                    stream.synchronize()
+                    lat.append(time.perf_counter() - t0)
+                res[key + "_isolated_step_us"].append(round(float(np.median(lat)) * 1e6, 1))
         graphs.close()
     stream.synchronize()
     return res
@@ -427,6 +436,8 @@ def main():
                     help="leave the long-context decode leg (161 GiB pool, about 14 GB of K/V per step) out of the step")
     ap.add_argument("--step-only", action="store_true",
                     help="skip the untimed host block-manager, decode-graph and cold-launch legs (profiling runs)")
+    ap.add_argument("--decode-graph-only", action="store_true",
+                    help="run only the eager-vs-graph decode-step leg and print its JSON (for a kernel trace of it)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, run one 256 MiB device copy (reads and writes a known byte count) "
                          "so that profiler byte counters can be calibrated against it")
@@ -437,6 +448,16 @@ def main():
                           "n_gpus": args.gpus}))
         sys.exit(2)
 
+    if args.decode_graph_only:
+        import torch
+
+        import paged_kv_cache_heads_amd as pa
+        from workloads import configs, tensors
+        wl2 = configs.config2()
+        b2 = tensors.materialize(wl2, torch.device("cuda:0"))
+        print(json.dumps({"decode_graph": decode_graph_latency(pa, torch, b2, wl2, 1.0 / math.sqrt(128))}),
+              flush=True)
+        return
     # the oracle's worker processes start before anything touches the GPU
     n_cores = host_cores()
     pool = None if args.no_cpu_baseline else start_oracle_pool(n_cores)

@@ -326,40 +326,44 @@ int pa_sample_gumbel(int32_t* tokens, const float* logits, int64_t logits_row_st
                      size_t workspace_bytes, void* stream);
 
 /*
- * Graph-captured decode steps (store of the new tokens + pa_decode), one HIP
- * graph per padded batch size, replayed with a single launch (page
- * "nano-vLLM 最小化vLLM重新实现", section 4 "模型运行器": decode graphs are
- * captured ahead of time at batch sizes 1, 2, 4, 8, 16, 32, ..., 512 and
- * replayed; page at bxzpzcl.cn/news/2159246, section 3.1: graphs remove the
- * per-step launch overhead).
+ * Graph-captured decode steps (pa_store_decode: the new tokens' store and the
+ * paged decode, two kernels), one HIP graph per padded batch size, each step
+ * replayed with a single graph launch (page "nano-vLLM 最小化vLLM重新实现",
+ * section 4 "模型运行器": decode graphs are captured ahead of time at batch
+ * sizes 1, 2, 4, 8, 16, 32, ..., 512 and replayed; page at
+ * bxzpzcl.cn/news/2159246, section 3.1: graphs remove the per-step launch
+ * overhead).
  *
  * pa_decode_step names the device buffers every captured graph reads and
  * writes, sized for the largest batch size: row i of q, k_new, v_new,
- * slot_mapping, block_tables, context_lens and out belongs to sequence i of the
- * step. The caller fills rows 0 .. batch - 1 before each launch; launch sets
- * rows batch .. padded - 1 to slot -1 and length 0 (nothing stored, zero
- * output rows). max_context_len bounds every context length of every launch;
- * workspace must hold pa_decode_workspace_size() for the largest batch size.
- * The buffers must stay allocated, and the struct's values fixed, while the
- * graphs exist.
+ * block_tables, context_lens and out belongs to sequence i of the step.
+ * Before each launch the caller fills rows 0 .. batch - 1 and writes batch to
+ * *live_batch (a device int32), together with the step's other inputs. The
+ * graph of padded size P treats rows batch .. P - 1 as empty contexts:
+ * nothing is stored for them, their output rows are zeros, and nothing else of
+ * theirs is read (their context_lens entries are read and ignored), so they
+ * need not be written. Results of rows 0 .. batch - 1 equal pa_store_decode at
+ * batch rows, bit for bit. max_context_len bounds every context length of
+ * every launch; workspace must hold pa_decode_workspace_size() for the
+ * largest batch size. The buffers must stay allocated, and the struct's values
+ * fixed, while the graphs exist.
  */
 typedef struct pa_decode_step {
-  void* q;                    /* [max_batch, num_q_heads, head_dim] bf16 */
+  const void* q;              /* [max_batch, num_q_heads, head_dim] bf16 */
   int64_t q_seq_stride;
   const void* k_new;          /* [max_batch, num_kv_heads, head_dim] bf16 */
   int64_t k_token_stride;
   const void* v_new;
   int64_t v_token_stride;
-  int32_t* slot_mapping;      /* [max_batch] */
+  const int32_t* live_batch;  /* one device int32: the batch of the next launch */
   const int32_t* block_tables; /* [max_batch, max_blocks_per_seq] */
   int32_t max_blocks_per_seq;
-  int32_t* context_lens;      /* [max_batch] */
+  const int32_t* context_lens; /* [max_batch] */
   void* out;                  /* [max_batch, num_q_heads, head_dim] bf16 */
   void* workspace;
   size_t workspace_bytes;
   void* k_cache;
   void* v_cache;
-  int64_t num_blocks;
   int32_t block_size;
   int32_t num_q_heads;
   int32_t num_kv_heads;
@@ -374,18 +378,20 @@ typedef struct pa_decode_graphs pa_decode_graphs;
 /*
  * Capture one graph per entry of batch_sizes (positive, strictly increasing,
  * at most 32 of them) on stream, which must not be the legacy default stream.
- * Each graph is pa_store_kvcache + pa_decode at that batch size with the
- * step's arguments; capturing launches nothing. Errors of the captured calls
- * are returned as they are (and nothing is kept); a failed capture returns
- * PA_ERR_HIP.
+ * Each graph is pa_store_decode at that batch size with the step's arguments
+ * and its live count; capturing launches nothing. Errors of the captured
+ * calls are returned as they are (and nothing is kept); a failed capture
+ * returns PA_ERR_HIP.
  */
 int pa_decode_graphs_create(const pa_decode_step* step, const int32_t* batch_sizes, int32_t count, void* stream,
                             pa_decode_graphs** out);
 
 /*
  * One decode step of batch sequences (1 <= batch <= the largest captured
- * size): pads rows batch .. padded - 1 and launches the graph of the smallest
- * captured size padded >= batch on stream. *padded (optional) receives it.
+ * size): one launch of the graph of the smallest captured size padded >=
+ * batch on stream. *live_batch must already hold batch on the device (written
+ * by the caller before this call, in stream order). *padded (optional)
+ * receives the padded size.
  */
 int pa_decode_graphs_launch(pa_decode_graphs* graphs, int32_t batch, void* stream, int32_t* padded);
 

@@ -358,17 +358,19 @@ def pa_prefill_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, ma
 
 
 class DecodeGraphs:
-    """Graph-captured decode steps (pa_decode_graphs_*): store + decode captured once per batch size.
+    """Graph-captured decode steps (pa_decode_graphs_*): pa_store_decode captured once per batch size.
 
     The tensors are the step's fixed device buffers, sized for max(batch_sizes): q [B, Hq, D],
-    k_new / v_new [B, Hkv, D] views, slot_mapping [B], block_tables [B, W], context_lens [B] (int32),
-    out [B, Hq, D], workspace (uint8, >= pa_decode_workspace_size for the largest batch). Fill rows
-    0 .. batch - 1, then launch(batch); rows past batch are padded by the library.
+    k_new / v_new [B, Hkv, D] views, block_tables [B, W], context_lens [B] (int32), out [B, Hq, D],
+    workspace (uint8, >= pa_decode_workspace_size for the largest batch). The binding also holds
+    `live_batch`, a one-element int32 device tensor. For each step fill rows 0 .. batch - 1 and write
+    batch to live_batch (or let launch() write it), then launch(batch): one graph launch; rows past
+    batch are empty contexts (zero output rows, nothing stored, not read).
     Capture needs a stream other than the legacy default stream (stream or the current torch stream).
     """
 
-    def __init__(self, q, k_new, v_new, slot_mapping, block_tables, context_lens, out, workspace, k_cache,
-                 v_cache, scale: float, max_context_len: int, batch_sizes, split_waves: int = 0, stream=None):
+    def __init__(self, q, k_new, v_new, block_tables, context_lens, out, workspace, k_cache, v_cache,
+                 scale: float, max_context_len: int, batch_sizes, split_waves: int = 0, stream=None):
         import ctypes
 
         if workspace is None:
@@ -376,43 +378,50 @@ class DecodeGraphs:
         if out is None:
             raise TypeError("out is required")
         _want(q, "q", _BF16, 3)
-        _want(slot_mapping, "slot_mapping", _I32, 1, True)
         sizes_list = [int(b) for b in batch_sizes]
         if not sizes_list or min(sizes_list) < 1:
             raise ValueError(f"batch_sizes must be positive, got {sizes_list}")
         rows = int(q.shape[0])
         if max(sizes_list) > rows:
             raise ValueError(f"the step buffers hold {rows} rows, fewer than the largest batch size {max(sizes_list)}")
-        _shape(slot_mapping, "slot_mapping", (rows,))
         dev = _decode_args(q, k_cache, v_cache, block_tables, context_lens, out, workspace, k_new, v_new, True)
-        _device(q=q, slot_mapping=slot_mapping)
         lib = _lib.load()
         self._lib = lib
         nb, bs, hkv, d = k_cache.shape
-        self._keep = (q, k_new, v_new, slot_mapping, block_tables, context_lens, out, workspace, k_cache, v_cache)
+        self.live_batch = torch.zeros(1, dtype=torch.int32, device=dev)
+        self._keep = (q, k_new, v_new, block_tables, context_lens, out, workspace, k_cache, v_cache)
         st = _lib.DecodeStep(
             q=_ptr(q), q_seq_stride=_rows(q, "q"), k_new=_ptr(k_new), k_token_stride=_rows(k_new, "k_new"),
-            v_new=_ptr(v_new), v_token_stride=_rows(v_new, "v_new"), slot_mapping=_ptr(slot_mapping),
+            v_new=_ptr(v_new), v_token_stride=_rows(v_new, "v_new"), live_batch=_ptr(self.live_batch),
             block_tables=_ptr(block_tables), max_blocks_per_seq=int(block_tables.shape[1]),
             context_lens=_ptr(context_lens), out=_ptr(out), workspace=_ptr(workspace),
             workspace_bytes=workspace.numel() * workspace.element_size(), k_cache=_ptr(k_cache),
-            v_cache=_ptr(v_cache), num_blocks=nb, block_size=bs, num_q_heads=int(q.shape[1]), num_kv_heads=hkv,
-            head_dim=d, scale=float(scale), max_context_len=int(max_context_len), split_waves=int(split_waves))
-        sizes = (ctypes.c_int32 * len(batch_sizes))(*[int(b) for b in batch_sizes])
+            v_cache=_ptr(v_cache), block_size=bs, num_q_heads=int(q.shape[1]), num_kv_heads=hkv, head_dim=d,
+            scale=float(scale), max_context_len=int(max_context_len), split_waves=int(split_waves))
+        sizes = (ctypes.c_int32 * len(sizes_list))(*sizes_list)
         h = ctypes.c_void_p()
         _check("pa_decode_graphs_create", lib.pa_decode_graphs_create(
-            ctypes.byref(st), sizes, len(batch_sizes), _stream(stream, q.device), ctypes.byref(h)))
+            ctypes.byref(st), sizes, len(sizes_list), _stream(stream, dev), ctypes.byref(h)))
         self._h = h
-        self.batch_sizes = [int(b) for b in batch_sizes]
-        self.device = q.device
+        self.batch_sizes = sizes_list
+        self.device = dev
 
-    def launch(self, batch: int, stream=None) -> int:
-        """One decode step of `batch` sequences; returns the padded batch size replayed."""
+    def launch(self, batch: int, stream=None, live_written: bool = False) -> int:
+        """One decode step of `batch` sequences; returns the padded batch size replayed.
+
+        Unless live_written, batch is first written to live_batch on the launch stream (one small
+        fill); a caller that writes it with the step's other inputs passes live_written=True, and
+        the step is then a single graph launch.
+        """
         import ctypes
 
+        s = _stream(stream, self.device)
+        if not live_written:
+            with torch.cuda.stream(torch.cuda.ExternalStream(s, device=self.device)):
+                self.live_batch.fill_(int(batch))
         padded = ctypes.c_int32(0)
-        _check("pa_decode_graphs_launch", self._lib.pa_decode_graphs_launch(
-            self._h, int(batch), _stream(stream, self.device), ctypes.byref(padded)))
+        _check("pa_decode_graphs_launch", self._lib.pa_decode_graphs_launch(self._h, int(batch), s,
+                                                                            ctypes.byref(padded)))
         return padded.value
 
     def close(self) -> None:

@@ -15,11 +15,10 @@ class DecodeStep(ctypes.Structure):
     """pa_decode_step of include/pa.h (same field order and types)."""
     _fields_ = [
         ("q", _vp), ("q_seq_stride", _i64), ("k_new", _vp), ("k_token_stride", _i64), ("v_new", _vp),
-        ("v_token_stride", _i64), ("slot_mapping", _vp), ("block_tables", _vp), ("max_blocks_per_seq", _i32),
+        ("v_token_stride", _i64), ("live_batch", _vp), ("block_tables", _vp), ("max_blocks_per_seq", _i32),
         ("context_lens", _vp), ("out", _vp), ("workspace", _vp), ("workspace_bytes", _sz), ("k_cache", _vp),
-        ("v_cache", _vp), ("num_blocks", _i64), ("block_size", _i32), ("num_q_heads", _i32),
-        ("num_kv_heads", _i32), ("head_dim", _i32), ("scale", _f32), ("max_context_len", _i32),
-        ("split_waves", _i32),
+        ("v_cache", _vp), ("block_size", _i32), ("num_q_heads", _i32), ("num_kv_heads", _i32), ("head_dim", _i32),
+        ("scale", _f32), ("max_context_len", _i32), ("split_waves", _i32),
     ]
 
 

@@ -259,6 +259,14 @@ __device__ __forceinline__ void compute_chunk(DecodeState<G>& st, const QRegs<G>
   }
 }
 
+// Sequences the call covers: num_seqs, or fewer when a device count is given
+// (a graph captured at a padded batch size, replayed for a smaller batch:
+// sequences at or past the count are empty contexts and their rows are never
+// read, except for their lengths, which are masked).
+__device__ __forceinline__ int live_seqs(const DecodeArgs& a) {
+  return a.live_seqs ? max(0, min(a.num_seqs, *a.live_seqs)) : a.num_seqs;
+}
+
 // ---- wave-wide helpers for the work split ----
 __device__ __forceinline__ int wave_sum_i32(int x) {
 #pragma unroll
@@ -296,11 +304,11 @@ __device__ __forceinline__ void load_q(QRegs<G>& q, const DecodeArgs& a, int b, 
 }
 
 // Next chunk in (sequence, kv head, chunk) order; skips empty sequences.
-__device__ __forceinline__ Pos next_pos(const Pos& p, const DecodeArgs& a, int ch) {
+__device__ __forceinline__ Pos next_pos(const Pos& p, const DecodeArgs& a, int ch, int ns) {
   if (p.k + 1 < p.nc) return Pos{p.b, p.g, p.k + 1, p.len, p.nc};
   if (p.g + 1 < a.num_kv_heads) return Pos{p.b, p.g + 1, 0, p.len, p.nc};
   Pos n{p.b + 1, 0, 0, 0, 0};
-  for (; n.b < a.num_seqs; ++n.b) {
+  for (; n.b < ns; ++n.b) {
     n.len = uniform(a.context_lens[n.b]);
     n.nc = chunks_of(n.len, ch);
     if (n.nc > 0) break;
@@ -383,8 +391,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(G >= 8 ? 1 :
   // the first 256 lengths are loaded once and serve both scans below
   int lu0[4];
   load4_lens(a.context_lens, lane * 4, a.num_seqs, lu0);
+  const int ns = live_seqs(a);
   int64_t total = 0;
-  for (int base = 0; base < a.num_seqs; base += 256) {
+  for (int base = 0; base < ns; base += 256) {
     int x = 0, lu[4];
     if (base == 0) {
 #pragma unroll
@@ -393,7 +402,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(G >= 8 ? 1 :
       load4_lens(a.context_lens, base + lane * 4, a.num_seqs, lu);
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) x += base + lane * 4 + u < a.num_seqs ? chunks_of(lu[u], CH) : 0;
+    for (int u = 0; u < 4; ++u) x += base + lane * 4 + u < ns ? chunks_of(lu[u], CH) : 0;
     total += uniform(wave_sum_i32(x));
   }
   total *= a.num_kv_heads;
@@ -404,7 +413,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(G >= 8 ? 1 :
   Pos cur{0, 0, 0, 0, 0};
   {
     int64_t run = 0;
-    for (int base = 0; base < a.num_seqs; base += 256) {
+    for (int base = 0; base < ns; base += 256) {
       int len[4], x[4], sum = 0, lu[4];
       if (base == 0) {
 #pragma unroll
@@ -415,7 +424,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(G >= 8 ? 1 :
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int b = base + lane * 4 + u;
-        len[u] = b < a.num_seqs ? lu[u] : 0;
+        len[u] = b < ns ? lu[u] : 0;
         x[u] = chunks_of(len[u], CH) * a.num_kv_heads;
         sum += x[u];
       }
@@ -465,7 +474,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(G >= 8 ? 1 :
       Pos nxt = cur;
       bool new_pair = false;
       if (more) {
-        nxt = next_pos(cur, a, CH);
+        nxt = next_pos(cur, a, CH, ns);
         new_pair = nxt.b != cur.b || nxt.g != cur.g;
         load_chunk(c1, a, nxt, row_bytes, lane_off, r, s);
       }
@@ -485,7 +494,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(G >= 8 ? 1 :
       Pos nxt = cur;
       bool new_pair = false;
       if (more) {
-        nxt = next_pos(cur, a, CH);
+        nxt = next_pos(cur, a, CH, ns);
         new_pair = nxt.b != cur.b || nxt.g != cur.g;
         load_chunk(c0, a, nxt, row_bytes, lane_off, r, s);
       }
@@ -514,13 +523,14 @@ __global__ __launch_bounds__(64) void decode_finalize_kernel(DecodeArgs a) {
   // of the sequences before it, and of all sequences, per kv head.
   int64_t before = 0, all = 0;
   int nc = 0;
-  for (int base = 0; base < a.num_seqs; base += 256) {
+  const int ns = live_seqs(a);  // rows at or past it are empty: zero output, nothing stored
+  for (int base = 0; base < ns; base += 256) {
     int xb = 0, xa = 0, xm = 0, lu[4];
     load4_lens(a.context_lens, base + lane * 4, a.num_seqs, lu);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int sq = base + lane * 4 + u;  // lanes past the end count 0
-      const int c = sq < a.num_seqs ? chunks_of(lu[u], CH) : 0;
+      const int c = sq < ns ? chunks_of(lu[u], CH) : 0;
       xa += c;
       xb += sq < b ? c : 0;
       xm += sq == b ? c : 0;
@@ -587,13 +597,15 @@ __global__ __launch_bounds__(64) void decode_finalize_kernel(DecodeArgs a) {
       o1[j] *= alpha;
       M[j] = mnew;
     }
-    // the pieces' rows, four pieces' loads in flight at a time, added in wave
-    // order (a piece with weight 0 is skipped; its slot may hold stale bits)
-    for (int i0 = 0; i0 < n; i0 += 4) {
-      float2 ov[4][G];
-      float fq[4][G];
+    // the pieces' rows, PR pieces' loads in flight at a time (64 registers of
+    // loads whatever G), added in wave order (a piece with weight 0 is
+    // skipped; its slot may hold stale bits)
+    constexpr int PR = G <= 2 ? 16 : 32 / G;
+    for (int i0 = 0; i0 < n; i0 += PR) {
+      float2 ov[PR][G];
+      float fq[PR][G];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int q = 0; q < PR; ++q) {
         const int i = min(i0 + q, n - 1);
         const int64_t si = __shfl(slot, i);
 #pragma unroll
@@ -603,7 +615,7 @@ __global__ __launch_bounds__(64) void decode_finalize_kernel(DecodeArgs a) {
         }
       }
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
+      for (int q = 0; q < PR; ++q)
 #pragma unroll
         for (int j = 0; j < G; ++j) {
           if (fq[q][j] != 0.f) {
@@ -634,23 +646,6 @@ static hipError_t launch_decode_g(const DecodeArgs& a, hipStream_t stream) {
 }
 
 int decode_chunk_tokens(int group) { return group <= 2 ? 32 : 16; }
-
-__global__ void pad_decode_rows_kernel(int32_t* slot_mapping, int32_t* context_lens, int32_t from, int32_t to) {
-  const int32_t i = from + (int32_t)(blockIdx.x * blockDim.x + threadIdx.x);
-  if (i < to) {
-    slot_mapping[i] = -1;
-    context_lens[i] = 0;
-  }
-}
-
-hipError_t launch_pad_decode_rows(int32_t* slot_mapping, int32_t* context_lens, int32_t from, int32_t to,
-                                  hipStream_t stream) {
-  if (to <= from) return hipSuccess;
-  const int32_t n = to - from;
-  pad_decode_rows_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream>>>(slot_mapping, context_lens,
-                                                                                      from, to);
-  return hipGetLastError();
-}
 
 hipError_t launch_decode(const DecodeArgs& a, int group, hipStream_t stream) {
   if (a.num_seqs == 0) return hipSuccess;

@@ -1,13 +1,14 @@
 // Graph-captured decode steps (include/pa.h, pa_decode_graphs_*): one HIP
-// graph per padded batch size holding the store of the step's new tokens and
-// the paged decode, replayed with one launch (page "nano-vLLM
-// 最小化vLLM重新实现", section 4 "模型运行器": decode graphs captured at batch
-// sizes 1, 2, 4, ..., 512; page at bxzpzcl.cn/news/2159246, section 3.1).
+// graph per padded batch size holding pa_store_decode (the new tokens' store
+// fused into the split kernel and its finalize pass), each step replayed with
+// one graph launch (page "nano-vLLM 最小化vLLM重新实现", section 4 "模型运行器":
+// decode graphs captured at batch sizes 1, 2, 4, ..., 512; page at
+// bxzpzcl.cn/news/2159246, section 3.1).
 //
-// Capture goes through the public entry points, so the graphs hold exactly
-// the kernels an eager step launches, with the step's fixed buffers baked in.
-// Padding rows past the real batch is a separate one-kernel launch ahead of
-// the graph, so the graph itself never depends on the batch.
+// The graphs hold exactly the kernels an eager pa_store_decode launches, with
+// the step's fixed buffers baked in and one more argument: a device count of
+// live sequences, which the caller writes with the step's inputs. Rows past it
+// are empty contexts inside the kernels, so no padding work runs at launch.
 #include <hip/hip_runtime.h>
 
 #include <vector>
@@ -32,20 +33,6 @@ struct pa_decode_graphs {
 using pa::fail;
 using pa::ok;
 
-namespace {
-
-// The eager step the graphs hold: store then decode, for the first batch rows.
-int eager_step(const pa_decode_step& s, int32_t batch, hipStream_t stream) {
-  int st = pa_store_kvcache(s.k_new, s.k_token_stride, s.v_new, s.v_token_stride, s.k_cache, s.v_cache,
-                            s.slot_mapping, batch, s.num_kv_heads, s.head_dim, s.num_blocks, s.block_size, stream);
-  if (st != PA_OK) return st;
-  return pa_decode(s.out, s.q, s.q_seq_stride, s.k_cache, s.v_cache, s.block_tables, s.max_blocks_per_seq,
-                   s.context_lens, batch, s.num_q_heads, s.num_kv_heads, s.head_dim, s.block_size,
-                   s.max_context_len, s.scale, s.split_waves, s.workspace, s.workspace_bytes, stream);
-}
-
-}  // namespace
-
 extern "C" {
 
 int pa_decode_graphs_create(const pa_decode_step* step, const int32_t* batch_sizes, int32_t count, void* stream,
@@ -58,8 +45,8 @@ int pa_decode_graphs_create(const pa_decode_step* step, const int32_t* batch_siz
     if (batch_sizes[i] <= 0 || (i > 0 && batch_sizes[i] <= batch_sizes[i - 1]))
       return fail(PA_ERR_INVALID_ARGUMENT, "batch_sizes must be positive and strictly increasing");
   if (!stream) return fail(PA_ERR_INVALID_ARGUMENT, "capture needs a stream other than the legacy default stream");
-  if (!step->slot_mapping || !step->context_lens)
-    return fail(PA_ERR_NULL_POINTER, "slot_mapping and context_lens are required");
+  if (!step->live_batch || !step->context_lens || !step->k_new || !step->v_new)
+    return fail(PA_ERR_NULL_POINTER, "live_batch, context_lens, k_new and v_new are required");
   hipStream_t s = static_cast<hipStream_t>(stream);
   pa_decode_graphs* g = new pa_decode_graphs();
   g->step = *step;
@@ -69,7 +56,7 @@ int pa_decode_graphs_create(const pa_decode_step* step, const int32_t* batch_siz
       delete g;
       return fail(PA_ERR_HIP, "hipStreamBeginCapture failed for batch %d", b);
     }
-    const int st = eager_step(g->step, b, s);
+    const int st = pa::store_decode_live(g->step, b, s);
     hipGraph_t graph = nullptr;
     const hipError_t e = hipStreamEndCapture(s, &graph);
     if (st != PA_OK || e != hipSuccess || !graph) {
@@ -99,9 +86,7 @@ int pa_decode_graphs_launch(pa_decode_graphs* g, int32_t batch, void* stream, in
   size_t i = 0;
   while (g->sizes[i] < batch) ++i;
   const int32_t p = g->sizes[i];
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = pa::launch_pad_decode_rows(g->step.slot_mapping, g->step.context_lens, batch, p, s);
-  if (e == hipSuccess) e = hipGraphLaunch(g->execs[i], s);
+  const hipError_t e = hipGraphLaunch(g->execs[i], static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PA_ERR_HIP, "decode graph launch: %s", hipGetErrorString(e));
   if (padded) *padded = p;
   return ok();

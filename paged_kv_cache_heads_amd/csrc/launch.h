@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+struct pa_decode_step;
+
 namespace pa {
 
 // Record the message of a failing call (pa_last_error) and return its status;
@@ -38,6 +40,7 @@ struct DecodeArgs {
   int64_t v_new_stride;
   float* ws_o;   // [num_waves * 2 slots, G, head_dim] partial outputs
   float* ws_ml;  // [num_waves * 2 slots, G, 2] (max, sum) of each partial
+  const int32_t* live_seqs;  // optional device count: sequences at or past it are empty (graph replays)
   int32_t max_blocks_per_seq;
   int32_t num_seqs;
   int32_t num_q_heads;
@@ -113,9 +116,10 @@ hipError_t launch_store_kvcache(const StoreArgs& a, hipStream_t stream);
 hipError_t launch_norm_rope_store(const NormRopeArgs& a, hipStream_t stream);
 // group = num_q_heads / num_kv_heads (1, 2, 4 or 8); head_dim is 128.
 hipError_t launch_decode(const DecodeArgs& a, int group, hipStream_t stream);
-// Rows [from, to) of a padded decode batch: slot -1 (store nothing), length 0 (zero output).
-hipError_t launch_pad_decode_rows(int32_t* slot_mapping, int32_t* context_lens, int32_t from, int32_t to,
-                                  hipStream_t stream);
+// pa_store_decode over the step's buffers at num_seqs rows, with the step's
+// device count of live sequences (rows at or past it are empty contexts); the
+// call graph-captured decode steps hold. Defined in pa_api.cpp.
+int store_decode_live(const struct pa_decode_step& s, int32_t num_seqs, hipStream_t stream);
 // Tokens per decode work chunk for a GQA group size.
 int decode_chunk_tokens(int group);
 // The library's static decode scratch: 2048 waves x 2 slots x 8 heads x

@@ -5,6 +5,8 @@
 
 #include <hip/hip_runtime.h>
 #include <math.h>
+
+#include <algorithm>
 #include <stdarg.h>
 #include <stdio.h>
 
@@ -72,6 +74,7 @@ int hip_status(hipError_t e, const char* what) {
 // (256 CUs, 8 resident decode waves each) busy, but no more than there are
 // chunks of work.
 constexpr int32_t kDecodeWaves = 2048;
+constexpr int64_t kMinChunksPerWave = 4;
 
 struct DecodeGeometry {
   int32_t num_waves;
@@ -86,7 +89,12 @@ bool decode_geometry(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads
   const int group = num_q_heads / num_kv_heads;
   const int ch = pa::decode_chunk_tokens(group);
   const int64_t max_chunks = (int64_t)num_seqs * num_kv_heads * ((max_context_len + ch - 1) / ch);
-  int64_t nw = split_waves > 0 ? split_waves : kDecodeWaves;
+  // Default: 2048 waves (8 per CU), but no fewer than kMinChunksPerWave chunks
+  // per wave by the length bound: a small batch spread over many more waves
+  // leaves every (sequence, kv head) pair in many short pieces, and merging
+  // them costs more than the split saves.
+  int64_t nw = split_waves > 0 ? split_waves
+                               : std::min<int64_t>(kDecodeWaves, (max_chunks + kMinChunksPerWave - 1) / kMinChunksPerWave);
   if (nw > max_chunks) nw = max_chunks;
   if (nw < 1) nw = 1;
   g->num_waves = (int32_t)nw;
@@ -273,7 +281,8 @@ static int decode_impl(void* out, const void* q, int64_t q_seq_stride, const voi
                        const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
                        int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                        int32_t block_size, int32_t max_context_len, float scale, int32_t split_waves, void* workspace,
-                       size_t workspace_bytes, void* stream, bool static_scratch = false) {
+                       size_t workspace_bytes, void* stream, bool static_scratch = false,
+                       const int32_t* live_seqs = nullptr) {
   if (num_seqs < 0) return fail(PA_ERR_INVALID_ARGUMENT, "num_seqs %d is negative", num_seqs);
   if (num_seqs > 65535) return fail(PA_ERR_UNSUPPORTED, "num_seqs %d exceeds 65535", num_seqs);
   int st = check_heads(num_q_heads, num_kv_heads, head_dim);
@@ -332,6 +341,7 @@ static int decode_impl(void* out, const void* q, int64_t q_seq_stride, const voi
   a.v_new = static_cast<const uint16_t*>(v_new);
   a.k_new_stride = k_new_stride;
   a.v_new_stride = v_new_stride;
+  a.live_seqs = live_seqs;
   a.ws_o = static_cast<float*>(workspace);
   a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + g.ws_o_bytes);
   a.max_blocks_per_seq = max_blocks_per_seq;
@@ -344,6 +354,17 @@ static int decode_impl(void* out, const void* q, int64_t q_seq_stride, const voi
   return hip_status(pa::launch_decode(a, num_q_heads / num_kv_heads, static_cast<hipStream_t>(stream)),
                     "decode launch");
 }
+
+namespace pa {
+
+int store_decode_live(const pa_decode_step& s, int32_t num_seqs, hipStream_t stream) {
+  return decode_impl(s.out, s.q, s.q_seq_stride, s.k_new, s.k_token_stride, s.v_new, s.v_token_stride, s.k_cache,
+                     s.v_cache, s.block_tables, s.max_blocks_per_seq, s.context_lens, num_seqs, s.num_q_heads,
+                     s.num_kv_heads, s.head_dim, s.block_size, s.max_context_len, s.scale, s.split_waves,
+                     s.workspace, s.workspace_bytes, stream, false, s.live_batch);
+}
+
+}  // namespace pa
 
 extern "C" {
 

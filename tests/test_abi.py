@@ -161,8 +161,13 @@ def test_decode_workspace_size(lib):
     # fewer chunks than waves: one wave per chunk at most (4 x 8 x ceil(200/32) = 224)
     assert lib.pa_decode_split_waves(4, 16, 8, 200, 256) == 224
     assert lib.pa_decode_workspace_size(4, 16, 8, 128, 200, 256) == 224 * 2 * 2 * 130 * 4
-    # G = 4: 16-token chunks
-    assert lib.pa_decode_split_waves(1, 32, 8, 100, 0) == 8 * 7
+    # G = 4: 16-token chunks; by default at least 4 chunks per wave by the length bound (1 x 8 x 7 = 56 -> 14)
+    assert lib.pa_decode_split_waves(1, 32, 8, 100, 0) == 14
+    # a small batch under the bound: 16 x 8 x 64 = 8192 chunks -> 2048 waves; 1 x 8 x 64 = 512 -> 128
+    assert lib.pa_decode_split_waves(16, 16, 8, 2048, 0) == 2048
+    assert lib.pa_decode_split_waves(1, 16, 8, 2048, 0) == 128
+    # an explicit split is taken as given (clamped to one chunk per wave)
+    assert lib.pa_decode_split_waves(1, 16, 8, 2048, 512) == 512
     assert lib.pa_decode_workspace_size(4, 16, 8, 64, 2048, 0) == 0    # unsupported head_dim
     assert lib.pa_decode_workspace_size(4, 16, 8, 128, 2048, -1) == 0  # bad split
     assert lib.pa_decode_split_waves(4, 16, 8, 2048, 100) == 100

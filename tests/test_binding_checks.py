@@ -181,11 +181,11 @@ def test_sampler_shape_mismatch(case):
 def test_decode_graphs_buffers_must_hold_the_largest_batch():
     a = _decode_ok(4)
     kv = _cpu((4, 8, 128), BF)
-    common = (a["q"], kv, kv, _cpu((4,), I32), a["block_tables"], a["context_lens"], _cpu((4, 16, 128), BF),
-              _cpu((1024,), U8), a["k_cache"], a["v_cache"], 0.1, 256)
+    common = (a["q"], kv, kv, a["block_tables"], a["context_lens"], _cpu((4, 16, 128), BF), _cpu((1024,), U8),
+              a["k_cache"], a["v_cache"], 0.1, 256)
     with pytest.raises(ValueError, match="largest batch"):
         pa.DecodeGraphs(*common, [2, 8])
     bad = list(common)
-    bad[3] = _cpu((3,), I32)  # slot_mapping shorter than the step buffers
-    with pytest.raises(ValueError, match="slot_mapping"):
+    bad[4] = _cpu((3,), I32)  # context_lens shorter than the step buffers
+    with pytest.raises(ValueError, match="context_lens"):
         pa.DecodeGraphs(*bad, [2, 4])

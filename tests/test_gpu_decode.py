@@ -137,3 +137,12 @@ def test_decode_nonpositive_scale(dev, scale):
     announce(f"decode scale {scale}")
     _run(configs.config1(), dev, scale=scale)
     _run(configs.config2(2), dev, seqs=range(0, 256, 17), split_waves=300, scale=scale)
+
+
+@pytest.mark.parametrize("group", [1, 2, 4, 8])
+def test_decode_pairs_cut_into_many_pieces(dev, group):
+    # one long context over thousands of waves: each (sequence, kv head) pair is cut into hundreds of
+    # pieces, which the finalize pass merges in batches of 64 and load rounds of 16 / 8 / 4 pieces
+    announce(f"decode many pieces G={group}")
+    wl = configs.decode_workload("pieces", [16384, 3, 700], 2 * group, 2, 72, seed=17)
+    _run(wl, dev, split_waves=3000)
