@@ -17,6 +17,7 @@ One step is one pass of the whole path over seeded synthetic batches:
   sampler leg      Gumbel-max sampling of one token for each of the 256 decode
                    sequences over a 151936-token vocabulary (fp32 logits).
 After the timed steps (outside them): the decode legs as two separate calls,
+the prefill legs as one fused store + prefill call against the separate pair,
 host timings of the C++ block manager, the wall-clock decode-step latency eager
 vs graph-captured at batch 1, 16 and 256, and the fp64 oracle timed on the
 host's cores over the decode, prefill, prefix and long-decode batches.
@@ -113,6 +114,42 @@ def separate_decode_leg(pa, torch, b, wl, scale, max_len, ws, out, steps, warmup
     return {"store_us": round(st * 1e3, 2), "decode_us": round(dt * 1e3, 2),
             "kv_GBs_leg": round(kv / ((st + dt) * 1e-3) / 1e9, 1),
             "decode_GBs": round(decode_bytes(wl)["total"] / (dt * 1e-3) / 1e9, 1)}
+
+
+def fused_store_prefill(pa, torch, scale, b3, wl3, b4, wl4, out3, out4, steps, warmup):
+    """The two prefill legs as one pa_store_prefill_varlen call against pa_store_kvcache + pa_prefill_varlen
+    (medians of event-timed calls, alternating, back to back as in the step)."""
+    legs = {
+        "varlen": (lambda: (pa.pa_store_kvcache(b3.k_new, b3.v_new, b3.k_cache, b3.v_cache, b3.slot_mapping),
+                            pa.pa_prefill_varlen(b3.q, b3.k_new, b3.v_new, b3.cu_seqlens_q, b3.cu_seqlens_k,
+                                                 wl3.max_seqlen_q, wl3.max_seqlen_k, scale, out=out3)),
+                   lambda: pa.pa_store_prefill_varlen(b3.q, b3.k_new, b3.v_new, b3.k_cache, b3.v_cache,
+                                                      b3.slot_mapping, b3.cu_seqlens_q, b3.cu_seqlens_k,
+                                                      wl3.max_seqlen_q, wl3.max_seqlen_k, scale, out=out3)),
+        "prefix": (lambda: (pa.pa_store_kvcache(b4.k_new, b4.v_new, b4.k_cache, b4.v_cache, b4.slot_mapping),
+                            pa.pa_prefill_varlen(b4.q, b4.k_cache, b4.v_cache, b4.cu_seqlens_q, b4.cu_seqlens_k,
+                                                 wl4.max_seqlen_q, wl4.max_seqlen_k, scale,
+                                                 block_table=b4.block_tables, out=out4)),
+                   lambda: pa.pa_store_prefill_varlen(b4.q, b4.k_new, b4.v_new, b4.k_cache, b4.v_cache,
+                                                      b4.slot_mapping, b4.cu_seqlens_q, b4.cu_seqlens_k,
+                                                      wl4.max_seqlen_q, wl4.max_seqlen_k, scale,
+                                                      block_table=b4.block_tables, out=out4)),
+    }
+    res = {}
+    for name, (unfused, fused) in legs.items():
+        t = {"unfused": [], "fused": []}
+        for i in range(warmup + steps):
+            for key, fn in (("unfused", unfused), ("fused", fused)):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                fn()
+                e1.record()
+                torch.cuda.synchronize()
+                if i >= warmup:
+                    t[key].append(e0.elapsed_time(e1) * 1e3)
+        res[name] = {"store_then_prefill_us": round(float(np.median(t["unfused"])), 2),
+                     "fused_us": round(float(np.median(t["fused"])), 2)}
+    return res
 
 
 def measured_peaks(torch, dev):
@@ -660,6 +697,8 @@ def run(args, pool, n_cores) -> dict:
         if b5 is not None:
             result["long_decode_separate_calls"] = separate_decode_leg(
                 pa, torch, b5, wl5, scale, wl5.max_context_len, ws5, out5, args.steps, args.warmup, args.split_waves)
+        result["store_prefill_fused"] = fused_store_prefill(pa, torch, scale, b3, wl3, b4, wl4, out3, out4,
+                                                            args.steps, args.warmup)
         result["host_block_manager"] = host_block_manager(wl2, wl4)
         result["decode_graph"] = decode_graph_latency(pa, torch, b2, wl2, scale)
     if pool is not None:

@@ -326,6 +326,53 @@ int pa_sample_gumbel(int32_t* tokens, const float* logits, int64_t logits_row_st
                      size_t workspace_bytes, void* stream);
 
 /*
+ * pa_store_prefill_varlen — the prefill step's store and pa_prefill_varlen in
+ * one call.
+ *
+ * Same results as pa_store_kvcache of the new tokens followed by
+ * pa_prefill_varlen (page "nano-vLLM 最小化vLLM重新实现", section 5 "注意力机制":
+ * the new tokens' K/V are written to the paged cache by slot_mapping, then
+ * varlen prefill attends over them, through the block table when a prefix is
+ * cached; page at hotelren.com/news/2273631, section 4.4). The new tokens are
+ * one per query: new token j of sequence i is row cu_seqlens_q[i] + j of
+ * k_new / v_new and is the key at position nk - nq + j; it is stored at
+ * slot_mapping[cu_seqlens_q[i] + j] (skipped when that slot is negative or at
+ * least num_blocks * block_size).
+ *
+ * block_table == NULL: every key is a new token, so each sequence must have
+ *   nk == nq (cu_seqlens_k equal to cu_seqlens_q); keys come from k_new /
+ *   v_new.
+ * block_table != NULL: keys 0 .. nk - nq - 1 come from the cache through the
+ *   table, keys nk - nq .. nk - 1 from k_new / v_new (they are not read back
+ *   from the cache). The result equals the unfused pair when every new
+ *   token's slot is its position through the table (slot = block_table[i,
+ *   p / block_size] * block_size + p % block_size), as a block manager makes
+ *   them; that is a precondition.
+ *
+ * The query tile of each work item stores its own tokens (each row is written
+ * once), after its attention, from the rows its last tiles just read. Cache
+ * bytes are bit-exact copies. Outputs are bit-identical to the unfused pair's
+ * at the same key tile; with a block table the fused call always runs 64-key
+ * tiles (pa_prefill_varlen picks 32-key tiles up to max_seqlen_k 1024), so
+ * there the two may differ by rounding only.
+ *
+ * k_new, v_new  [total_q, num_kv_heads, head_dim] bf16, heads x dims
+ *               contiguous, rows k_new_stride / v_new_stride elements apart.
+ * k_cache, v_cache  [num_blocks, block_size, num_kv_heads, head_dim]: written
+ *               at the new tokens' slots; read through block_table if given.
+ * slot_mapping  [total_q] int32.
+ * num_blocks    positive, num_blocks * block_size < 2^31.
+ * Every other argument, and the errors, as in pa_prefill_varlen.
+ */
+int pa_store_prefill_varlen(void* out, const void* q, int64_t q_token_stride, const void* k_new,
+                            int64_t k_new_stride, const void* v_new, int64_t v_new_stride, void* k_cache,
+                            void* v_cache, const int32_t* slot_mapping, const int32_t* cu_seqlens_q,
+                            const int32_t* cu_seqlens_k, int32_t num_seqs, int32_t max_seqlen_q,
+                            int32_t max_seqlen_k, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                            float scale, int32_t causal, const int32_t* block_table, int32_t max_blocks_per_seq,
+                            int32_t block_size, int64_t num_blocks, void* stream);
+
+/*
  * Graph-captured decode steps (pa_store_decode: the new tokens' store and the
  * paged decode, two kernels), one HIP graph per padded batch size, each step
  * replayed with a single graph launch (page "nano-vLLM 最小化vLLM重新实现",

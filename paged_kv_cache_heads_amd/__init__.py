@@ -19,6 +19,7 @@ __all__ = [
     "PAError", "LibraryMissing", "pa_store_kvcache", "pa_qk_norm_rope_store", "pa_decode", "pa_store_decode",
     "pa_decode_workspace_size", "pa_decode_split_waves", "pa_prefill_varlen", "pa_status_string", "pa_last_error", "pa_version",
     "library_path", "DecodeGraphs", "pa_sample_gumbel", "pa_sample_workspace_size", "pa_store_decode_noalloc",
+    "pa_store_prefill_varlen",
 ]
 
 
@@ -354,6 +355,49 @@ def pa_prefill_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, ma
         _ptr(out), _ptr(q), _rows(q, "q"), _ptr(k), _ptr(v), ks, vs, _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
         num_seqs, int(max_seqlen_q), int(max_seqlen_k), hq, hkv, d, float(scale), 1 if causal else 0,
         _ptr(block_table), width, bs, _stream(stream, dev)))
+    return out
+
+
+def pa_store_prefill_varlen(q, k_new, v_new, k_cache, v_cache, slot_mapping, cu_seqlens_q, cu_seqlens_k,
+                            max_seqlen_q: int, max_seqlen_k: int, scale: float, causal: bool = True, block_table=None,
+                            out=None, stream=None):
+    """Store the new tokens (k_new / v_new [Tq, Hkv, D], one per query, at slot_mapping [Tq]) and run the
+    varlen prefill in one call: q [Tq, Hq, D] -> out [Tq, Hq, D] bf16. Without block_table every key is
+    new (nk == nq); with it, keys before the new tokens come from the caches through the table."""
+    _want(q, "q", _BF16, 3)
+    _want(k_new, "k_new", _BF16, 3)
+    _want(v_new, "v_new", _BF16, 3)
+    _want(k_cache, "k_cache", _BF16, 4, True)
+    _want(v_cache, "v_cache", _BF16, 4, True)
+    _want(slot_mapping, "slot_mapping", _I32, 1, True)
+    _want(cu_seqlens_q, "cu_seqlens_q", _I32, 1, True)
+    _want(cu_seqlens_k, "cu_seqlens_k", _I32, 1, True)
+    _want(block_table, "block_table", _I32, 2, True, optional=True)
+    _want(out, "out", _BF16, 3, True, optional=True)
+    tq, hq, d = (int(x) for x in q.shape)
+    nb, bs, hkv, _ = (int(x) for x in k_cache.shape)
+    num_seqs = int(cu_seqlens_q.shape[0]) - 1
+    if num_seqs < 0:
+        raise ValueError("cu_seqlens_q must hold num_seqs + 1 >= 1 offsets")
+    _shape(v_cache, "v_cache", k_cache.shape)
+    _shape(k_cache, "k_cache", (None, None, None, d))
+    _shape(k_new, "k_new", (tq, hkv, d))
+    _shape(v_new, "v_new", (tq, hkv, d))
+    _shape(slot_mapping, "slot_mapping", (tq,))
+    _shape(cu_seqlens_k, "cu_seqlens_k", cu_seqlens_q.shape)
+    _shape(block_table, "block_table", (num_seqs, None))
+    _shape(out, "out", q.shape)
+    dev = _device(q=q, k_new=k_new, v_new=v_new, k_cache=k_cache, v_cache=v_cache, slot_mapping=slot_mapping,
+                  cu_seqlens_q=cu_seqlens_q, cu_seqlens_k=cu_seqlens_k, block_table=block_table, out=out)
+    lib = _lib.load()
+    if out is None:
+        out = torch.empty((tq, hq, d), dtype=torch.bfloat16, device=dev)
+    width = 0 if block_table is None else int(block_table.shape[1])
+    _check("pa_store_prefill_varlen", lib.pa_store_prefill_varlen(
+        _ptr(out), _ptr(q), _rows(q, "q"), _ptr(k_new), _rows(k_new, "k_new"), _ptr(v_new), _rows(v_new, "v_new"),
+        _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), num_seqs,
+        int(max_seqlen_q), int(max_seqlen_k), hq, hkv, d, float(scale), 1 if causal else 0, _ptr(block_table), width,
+        bs, nb, _stream(stream, dev)))
     return out
 
 

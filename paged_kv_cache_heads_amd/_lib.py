@@ -39,6 +39,9 @@ SIGNATURES = {
                                                _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp]),
     "pa_prefill_varlen": (ctypes.c_int, [_vp, _vp, _i64, _vp, _vp, _i64, _i64, _i32p, _i32p, _i32, _i32, _i32, _i32,
                                          _i32, _i32, _f32, _i32, _i32p, _i32, _i32, _vp]),
+    "pa_store_prefill_varlen": (ctypes.c_int, [_vp, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _i32p, _i32p, _i32p,
+                                               _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32p, _i32, _i32, _i64,
+                                               _vp]),
     "pa_sample_workspace_size": (_sz, [_i32, _i32]),
     "pa_sample_gumbel": (ctypes.c_int, [_vp, _vp, _i64, _vp, _i32, _i32, ctypes.c_uint64, ctypes.c_uint64, _vp, _sz,
                                         _vp]),

@@ -71,6 +71,18 @@ struct PrefillArgs {
   int32_t num_kv_heads;
   int32_t causal;
   float scale_log2e;
+  // fused store (pa_store_prefill_varlen), else null: new token j of sequence
+  // i is row cu_seqlens_q[i] + j of k_new / v_new (the key at position
+  // nk - nq + j), stored at slot_mapping of that row unless the slot is
+  // negative or at least store_capacity
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  int64_t k_new_stride;  // elements
+  int64_t v_new_stride;
+  const int32_t* slot_mapping;
+  uint16_t* k_cache_out;
+  uint16_t* v_cache_out;
+  int64_t store_capacity;  // num_blocks * block_size
 };
 
 struct NormRopeArgs {

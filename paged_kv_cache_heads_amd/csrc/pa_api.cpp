@@ -402,11 +402,27 @@ int pa_store_decode_noalloc(void* out, const void* q, int64_t q_seq_stride, cons
                      max_context_len, scale, split_waves, nullptr, 0, stream, /*static_scratch=*/true);
 }
 
-int pa_prefill_varlen(void* out, const void* q, int64_t q_token_stride, const void* k, const void* v,
-                      int64_t k_token_stride, int64_t v_token_stride, const int32_t* cu_seqlens_q,
-                      const int32_t* cu_seqlens_k, int32_t num_seqs, int32_t max_seqlen_q, int32_t max_seqlen_k,
-                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, float scale, int32_t causal,
-                      const int32_t* block_table, int32_t max_blocks_per_seq, int32_t block_size, void* stream) {
+}  // extern "C"
+
+// Argument checks and launch of the prefill kernel; st (optional) asks for the
+// fused store of pa_store_prefill_varlen.
+struct PrefillStore {
+  const void* k_new;
+  const void* v_new;
+  int64_t k_new_stride, v_new_stride;
+  void* k_cache;
+  void* v_cache;
+  const int32_t* slot_mapping;
+  int64_t num_blocks;
+  int32_t block_size_for_capacity;
+};
+
+static int prefill_impl(void* out, const void* q, int64_t q_token_stride, const void* k, const void* v,
+                        int64_t k_token_stride, int64_t v_token_stride, const int32_t* cu_seqlens_q,
+                        const int32_t* cu_seqlens_k, int32_t num_seqs, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                        int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, float scale, int32_t causal,
+                        const int32_t* block_table, int32_t max_blocks_per_seq, int32_t block_size, void* stream,
+                        const PrefillStore* st_args = nullptr) {
   if (num_seqs < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
     return fail(PA_ERR_INVALID_ARGUMENT, "num_seqs (%d), max_seqlen_q (%d) and max_seqlen_k (%d) must be >= 0",
                 num_seqs, max_seqlen_q, max_seqlen_k);
@@ -471,7 +487,66 @@ int pa_prefill_varlen(void* out, const void* q, int64_t q_token_stride, const vo
   a.num_kv_heads = num_kv_heads;
   a.causal = causal ? 1 : 0;
   a.scale_log2e = scale * kLog2e;
+  a.k_new = a.v_new = nullptr;
+  a.k_new_stride = a.v_new_stride = 0;
+  a.slot_mapping = nullptr;
+  a.k_cache_out = a.v_cache_out = nullptr;
+  a.store_capacity = 0;
+  if (st_args) {
+    a.k_new = static_cast<const uint16_t*>(st_args->k_new);
+    a.v_new = static_cast<const uint16_t*>(st_args->v_new);
+    a.k_new_stride = st_args->k_new_stride;
+    a.v_new_stride = st_args->v_new_stride;
+    a.slot_mapping = st_args->slot_mapping;
+    a.k_cache_out = static_cast<uint16_t*>(st_args->k_cache);
+    a.v_cache_out = static_cast<uint16_t*>(st_args->v_cache);
+    a.store_capacity = st_args->num_blocks * (int64_t)st_args->block_size_for_capacity;
+  }
   return hip_status(pa::launch_prefill(a, group, static_cast<hipStream_t>(stream)), "prefill launch");
+}
+
+extern "C" {
+
+int pa_prefill_varlen(void* out, const void* q, int64_t q_token_stride, const void* k, const void* v,
+                      int64_t k_token_stride, int64_t v_token_stride, const int32_t* cu_seqlens_q,
+                      const int32_t* cu_seqlens_k, int32_t num_seqs, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, float scale, int32_t causal,
+                      const int32_t* block_table, int32_t max_blocks_per_seq, int32_t block_size, void* stream) {
+  return prefill_impl(out, q, q_token_stride, k, v, k_token_stride, v_token_stride, cu_seqlens_q, cu_seqlens_k,
+                      num_seqs, max_seqlen_q, max_seqlen_k, num_q_heads, num_kv_heads, head_dim, scale, causal,
+                      block_table, max_blocks_per_seq, block_size, stream);
+}
+
+int pa_store_prefill_varlen(void* out, const void* q, int64_t q_token_stride, const void* k_new,
+                            int64_t k_new_stride, const void* v_new, int64_t v_new_stride, void* k_cache,
+                            void* v_cache, const int32_t* slot_mapping, const int32_t* cu_seqlens_q,
+                            const int32_t* cu_seqlens_k, int32_t num_seqs, int32_t max_seqlen_q,
+                            int32_t max_seqlen_k, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                            float scale, int32_t causal, const int32_t* block_table, int32_t max_blocks_per_seq,
+                            int32_t block_size, int64_t num_blocks, void* stream) {
+  const int64_t kv_row = (int64_t)num_kv_heads * head_dim;
+  int st = check_block_size(block_size);
+  if (st) return st;
+  if (num_blocks <= 0 || num_blocks > ((int64_t)1 << 31) / block_size)
+    return fail(PA_ERR_INVALID_ARGUMENT, "num_blocks %lld must be positive with num_blocks * block_size < 2^31",
+                (long long)num_blocks);
+  if (num_seqs > 0 && max_seqlen_q > 0) {
+    if (!k_new || !v_new || !k_cache || !v_cache || !slot_mapping)
+      return fail(PA_ERR_NULL_POINTER, "k_new, v_new, k_cache, v_cache and slot_mapping are required");
+    if (k_new_stride < kv_row || v_new_stride < kv_row)
+      return fail(PA_ERR_INVALID_ARGUMENT, "k_new / v_new strides (%lld, %lld) are below a row (%lld)",
+                  (long long)k_new_stride, (long long)v_new_stride, (long long)kv_row);
+    if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache) || k_new_stride % 8 ||
+        v_new_stride % 8)
+      return fail(PA_ERR_ALIGNMENT, "k_new, v_new, the caches and the strides must be 16-byte aligned");
+  }
+  PrefillStore sa{k_new, v_new, k_new_stride, v_new_stride, k_cache, v_cache, slot_mapping, num_blocks, block_size};
+  // without a block table the keys are the new tokens themselves (packed like the queries)
+  const void* k = block_table ? static_cast<const void*>(k_cache) : k_new;
+  const void* v = block_table ? static_cast<const void*>(v_cache) : v_new;
+  return prefill_impl(out, q, q_token_stride, k, v, k_new_stride, v_new_stride, cu_seqlens_q, cu_seqlens_k, num_seqs,
+                      max_seqlen_q, max_seqlen_k, num_q_heads, num_kv_heads, head_dim, scale, causal, block_table,
+                      max_blocks_per_seq, block_size, stream, &sa);
 }
 
 }  // extern "C"

@@ -133,7 +133,7 @@ __device__ __forceinline__ float max_xor32(float x) {
 // scaled first. BN: keys per tile, 64 (2 waves per SIMD) or 32 (half the
 // score registers and LDS, 3 waves per SIMD: finer causal steps and more
 // latency hiding for short sequences).
-template <int G, bool kRawMax, int BN>
+template <int G, bool kRawMax, int BN, bool kStore>
 __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(BN == 32 ? 3 : 2, 8)))
 void prefill_kernel(PrefillArgs a) {
   constexpr int kBN = BN;
@@ -284,6 +284,39 @@ void prefill_kernel(PrefillArgs a) {
     const char* vb = reinterpret_cast<const char*>(a.v + vrow0 + kvh * kPD);
     char* vdst = kdst + kTileBytes;
     const int last = nk - 1 - t0;  // rows past it are clamped to it (t0 < nk, so last >= 0)
+    if constexpr (kStore && BN == 64) {  // the fused store through a table always runs 64-key tiles
+      if (a.block_table != nullptr && t0 + kBN > shift) {
+        // Fused store through a block table: keys at positions >= shift are
+        // the new tokens, not in the cache yet; their rows come from k_new /
+        // v_new (row q_beg + position - shift). A tile that starts below shift
+        // takes its first rows from the cache as above (two passes, each lane
+        // in the one that holds its row; extra instructions only make the
+        // tile waits stricter).
+        const int nrow0 = max(t0 - shift, 0);  // first new-token row the tile needs
+        const char* nkb = reinterpret_cast<const char*>(a.k_new + (int64_t)(q_beg + nrow0) * a.k_new_stride + kvh * kPD);
+        const char* nvb = reinterpret_cast<const char*>(a.v_new + (int64_t)(q_beg + nrow0) * a.v_new_stride + kvh * kPD);
+        const uint32_t kch = ((lane & 15) ^ (srow0 & 15)) << 4;
+        const uint32_t vch = ((lane & 15) ^ ((srow0 & 7) << 1)) << 4;
+#pragma unroll
+        for (int u = 0; u < DU; ++u) {
+          const int row = min(srow0 + 16 * u, last);
+          const int o = (16 * u + 4 * wave) * 256;
+          const int nr = t0 + row - shift - nrow0;  // row within the tile's new-token rows (< kBN)
+          if (nr >= 0) {
+            __builtin_amdgcn_global_load_lds(nkb + (uint32_t)(nr * a.k_new_stride * 2) + kch,
+                                             (lds_void_t*)(kdst + o), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(nvb + (uint32_t)(nr * a.v_new_stride * 2) + vch,
+                                             (lds_void_t*)(vdst + o), 16, 0, 0);
+          } else {
+            __builtin_amdgcn_global_load_lds(kb + (uint32_t)(row * kstride * 2) + kch, (lds_void_t*)(kdst + o),
+                                             16, 0, 0);
+            __builtin_amdgcn_global_load_lds(vb + (uint32_t)(row * vstride * 2) + vch, (lds_void_t*)(vdst + o),
+                                             16, 0, 0);
+          }
+        }
+        return;
+      }
+    }
     // byte offsets from the tile's first row (below 2^31: checked on the host);
     // a clamped row keeps its lane's swizzled chunk, selected without a branch
     const uint32_t kcl = (uint32_t)(last * kstride * 2) + (((lane & 15) ^ (srow0 & 15)) << 4);
@@ -460,6 +493,32 @@ void prefill_kernel(PrefillArgs a) {
       if (tile + 2 < ntiles) step(tile + 2, Buf<2>());
   }
 
+  // ---- fused store, first half: load this item's new tokens' K and V rows of kv head kvh ----
+  // New token j of the sequence (one per query) is row q_beg + j of k_new / v_new. The item of query
+  // tile j / QP stores it, so every row is written once. The rows were just read by this item's last
+  // tiles, so the loads are served by L2; they are issued here so that their latency overlaps the
+  // output epilogue. 32 vectors of 16 bytes per token (K then V).
+  constexpr int kVecs = kStore ? QP * 32 / kPThreads : 1;  // vectors per thread
+  uint4 sval[kVecs];
+  int sslot[kVecs];
+  if constexpr (kStore) {
+    const int ntok = min(QP, nq - q0);
+#pragma unroll
+    for (int i = 0; i < kVecs; ++i) {
+      const int v = tid + i * kPThreads;
+      const int j = v >> 5, c = v & 31;
+      sslot[i] = -1;
+      if (j < ntok) {
+        const int64_t row = q_beg + q0 + j;
+        const int s = a.slot_mapping[row];
+        const uint16_t* src = (c >= 16 ? a.v_new + row * a.v_new_stride : a.k_new + row * a.k_new_stride) +
+                              kvh * kPD + (c & 15) * 8;
+        sval[i] = load16(src);
+        sslot[i] = s >= 0 && s < a.store_capacity ? s : -1;
+      }
+    }
+  }
+
   // ---- epilogue: normalise and write the rows that exist ----
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
@@ -475,21 +534,43 @@ void prefill_kernel(PrefillArgs a) {
       *reinterpret_cast<uint2*>(orow + dt * 16 + 4 * g) = w;
     }
   }
+
+  // ---- fused store, second half: the rows to their slots ----
+  if constexpr (kStore) {
+#pragma unroll
+    for (int i = 0; i < kVecs; ++i) {
+      if (sslot[i] >= 0) {
+        const int c = (tid + i * kPThreads) & 31;
+        uint16_t* cache = c >= 16 ? a.v_cache_out : a.k_cache_out;
+        store16_nt(cache + (int64_t)sslot[i] * a.num_kv_heads * kPD + kvh * kPD + (c & 15) * 8, sval[i]);
+      }
+    }
+  }
+}
+
+template <int G, int BN, bool kStore>
+static void launch_prefill_gbs(const PrefillArgs& a, hipStream_t stream) {
+  // one workgroup per work item, 8 XCD slices of items_per_xcd each
+  dim3 grid((unsigned)(8 * a.items_per_xcd));
+  if (a.scale_log2e > 0.f)
+    prefill_kernel<G, true, BN, kStore><<<grid, dim3(kPThreads), 0, stream>>>(a);
+  else
+    prefill_kernel<G, false, BN, kStore><<<grid, dim3(kPThreads), 0, stream>>>(a);
 }
 
 template <int G, int BN>
 static void launch_prefill_gb(const PrefillArgs& a, hipStream_t stream) {
-  // one workgroup per work item, 8 XCD slices of items_per_xcd each
-  dim3 grid((unsigned)(8 * a.items_per_xcd));
-  if (a.scale_log2e > 0.f)
-    prefill_kernel<G, true, BN><<<grid, dim3(kPThreads), 0, stream>>>(a);
+  if (a.slot_mapping)
+    launch_prefill_gbs<G, BN, true>(a, stream);
   else
-    prefill_kernel<G, false, BN><<<grid, dim3(kPThreads), 0, stream>>>(a);
+    launch_prefill_gbs<G, BN, false>(a, stream);
 }
 
 template <int G>
 static hipError_t launch_prefill_g(const PrefillArgs& a, hipStream_t stream) {
-  if (prefill_key_tile(a.max_seqlen_k) == 32)
+  // the fused store through a block table runs 64-key tiles (its per-row
+  // source choice does not fit the 32-key kernel's registers)
+  if (prefill_key_tile(a.max_seqlen_k) == 32 && !(a.slot_mapping && a.block_table))
     launch_prefill_gb<G, 32>(a, stream);
   else
     launch_prefill_gb<G, 64>(a, stream);

@@ -154,6 +154,31 @@ def test_store_decode_noalloc_validation(lib):
     assert "static scratch" in pa.pa_last_error()
 
 
+def store_prefill(lib, **kw):
+    a = dict(out=A, q=A, qs=2048, kn=A, kns=1024, vn=A, vns=1024, kc=A, vc=A, sl=A, cq=A, ck=A, S=4, maxq=1024,
+             maxk=1024, hq=16, hkv=8, d=128, scale=0.088, causal=1, bt=None, W=0, bs=256, nb=16, stream=None)
+    a.update(kw)
+    return lib.pa_store_prefill_varlen(a["out"], a["q"], a["qs"], a["kn"], a["kns"], a["vn"], a["vns"], a["kc"],
+                                       a["vc"], a["sl"], a["cq"], a["ck"], a["S"], a["maxq"], a["maxk"], a["hq"],
+                                       a["hkv"], a["d"], a["scale"], a["causal"], a["bt"], a["W"], a["bs"], a["nb"],
+                                       a["stream"])
+
+
+def test_store_prefill_validation(lib):
+    assert store_prefill(lib, sl=None) == NULLP
+    assert store_prefill(lib, kc=None) == NULLP
+    assert store_prefill(lib, kns=512) == INVAL        # below a row
+    assert store_prefill(lib, vns=1028) == ALIGN       # not 16-byte aligned
+    assert store_prefill(lib, kn=A + 2) == ALIGN
+    assert store_prefill(lib, nb=0) == INVAL
+    assert store_prefill(lib, nb=(1 << 23) + 1) == INVAL  # num_blocks * block_size > 2^31
+    assert store_prefill(lib, bs=96) == UNSUP
+    assert store_prefill(lib, hq=20) == INVAL           # the prefill checks apply too
+    assert store_prefill(lib, bt=A, W=3, maxk=1024) == INVAL
+    assert store_prefill(lib, S=0, out=None, q=None, kn=None, vn=None, kc=None, vc=None, sl=None, cq=None,
+                         ck=None) == PA_OK
+
+
 def test_decode_workspace_size(lib):
     # G = 2: 32-token chunks; 256 seqs x 8 kv heads x 64 chunks leave the default 2048 waves
     assert lib.pa_decode_split_waves(256, 16, 8, 2048, 0) == 2048
