@@ -303,11 +303,12 @@ int pa_prefill_varlen(void* out, const void* q, int64_t q_token_stride, const vo
  * T = max(temperatures[b], 1e-10):
  *   tokens[b] = argmax_i softmax(l / T)_i / E_i,  E_i = -ln(u_i),
  * which draws token i with probability softmax(l / T)_i. u_i comes from
- * Philox4x64-10 (Salmon et al., SC 2011) under key (seed, 0): element i takes
- * a 21-bit field w of 64-bit word (i / 3) % 4 of the block at counter
- * (i / 12, b, offset, 0) -- bits 63..43, 42..22 or 21..1 for i % 3 = 0, 1,
- * 2 -- and u = (w + 1/2) / 2^21. Pass a new offset (e.g. the step number) for new
- * noise. The decision is taken in fp32 (l log2(e) / T - log2(-log2(u))); ties
+ * Philox4x32-10 (Salmon et al., SC 2011) under key (seed mod 2^32, seed div
+ * 2^32): element i takes field i % 6 of the block at counter (i / 6, b,
+ * offset mod 2^32, offset div 2^32). The block's 32-bit words w0..w3 form
+ * X0 = w1:w0 and X1 = w3:w2; fields 0, 1, 2 are bits 63..43, 42..22, 21..1 of
+ * X0 and fields 3, 4, 5 the same bits of X1; a field w gives u = (w + 1/2) /
+ * 2^21. Pass a new offset (e.g. the step number) for new noise. The decision is taken in fp32 (l log2(e) / T - log2(-log2(u))); ties
  * go to the lowest index; -inf logits are never drawn unless a whole row is
  * -inf (then token 0 by the tie rule); NaN logits give an unspecified token in
  * [0, vocab_size).

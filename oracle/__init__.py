@@ -30,7 +30,7 @@ no blocking, fusion or reordering:
   preemption (page "nano-vLLM 最小化vLLM重新实现", section 3 "块管理器").
 
 * the Gumbel-max sampler (``sampler.sample``): argmax of softmax(l / T) over
-  exponential noise drawn with Philox4x64-10 (page "nano-vLLM
+  exponential noise drawn with Philox4x32-10 (page "nano-vLLM
   最小化vLLM重新实现", "辅助层" and "关键设计选择").
 
 Every function here is pinned by ``tests/test_oracle.py``,

@@ -1,47 +1,76 @@
 """Checks that pin the Gumbel-max sampler oracle to facts other than itself.
 
-Each ``check_*`` takes a module exposing ``philox4x64``, ``uniforms``,
+Each ``check_*`` takes a module exposing ``philox4x32``, ``uniforms``,
 ``scores`` and ``sample`` (the real ``oracle.sampler`` or a mutant). The
-facts: numpy's own Philox4x64-10 generator, the stated word-to-uniform map
-applied to numpy's words, the literal definition argmax softmax(l/T)/E with
-scipy's softmax, token frequencies that must follow softmax(l/T) (chi-square),
-and the limits of a dominant logit and of a small temperature.
+facts: rocRAND's Philox4x32-10 engine (its header, compiled here for the host:
+an independent implementation of the same generator), the stated
+word-to-uniform map applied to rocRAND's words, the literal definition
+argmax softmax(l/T)/E with scipy's softmax, token frequencies that must follow
+softmax(l/T) (chi-square), and the limits of a dominant logit and of a small
+temperature.
 """
 
 from __future__ import annotations
+
+import functools
+import os
+import shutil
+import subprocess
+import tempfile
 
 import numpy as np
 import scipy.special
 import scipy.stats
 
-
-def _numpy_block(counter, key):
-    """numpy's Philox4x64-10 block at `counter` (numpy steps the counter before each block)."""
-    c = [int(x) for x in counter]
-    c[0] -= 1
-    return np.random.Philox(counter=c, key=[int(k) for k in key]).random_raw(4)
+_HERE = os.path.dirname(os.path.abspath(__file__))
 
 
-def check_philox_matches_numpy(orc, seed=0):
+@functools.lru_cache(maxsize=1)
+def _reference_binary() -> str:
+    """Build tests/philox_ref.cpp (rocRAND's header engine, host code) once per session."""
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    out = os.path.join(tempfile.mkdtemp(prefix="philox_ref_"), "philox_ref")
+    subprocess.run([hipcc, "-O1", "-x", "hip", "--offload-arch=gfx950", os.path.join(_HERE, "philox_ref.cpp"),
+                    "-o", out], check=True, capture_output=True, timeout=300)
+    return out
+
+
+def reference_blocks(triples):
+    """rocRAND's Philox4x32-10 block for each (seed, subsequence, c): counter (c lo, c hi, sub lo, sub hi),
+    key (seed lo, seed hi). Returns uint64 [n, 4] holding 32-bit words."""
+    text = "".join(f"{int(s)} {int(u)} {int(c)}\n" for s, u, c in triples)
+    res = subprocess.run([_reference_binary()], input=text, capture_output=True, text=True, check=True, timeout=60)
+    return np.array([[int(w) for w in line.split()] for line in res.stdout.splitlines()], dtype=np.uint64)
+
+
+def check_philox_matches_rocrand(orc, seed=0):
     rng = np.random.default_rng(seed)
-    for _ in range(20):
-        ctr = rng.integers(1, 2 ** 63, 4, dtype=np.uint64)
-        key = rng.integers(0, 2 ** 63, 2, dtype=np.uint64)
-        got = orc.philox4x64(ctr[None, :], key[None, :])[0]
-        assert np.array_equal(got, _numpy_block(ctr, key))
+    triples = [(int(rng.integers(0, 2 ** 63)) * 2 + int(rng.integers(0, 2)), int(rng.integers(0, 2 ** 63)),
+                int(rng.integers(0, 2 ** 62))) for _ in range(24)]
+    # (the engine skips 4 c numbers in a 64-bit count, so c stays below 2^62)
+    triples += [(0, 0, 0), (2 ** 64 - 1, 2 ** 64 - 1, 2 ** 62 - 1), (1, 2 ** 32 + 5, 2 ** 32 - 1)]
+    want = reference_blocks(triples)
+    for (sd, sub, c), w in zip(triples, want):
+        ctr = np.array([[c % 2 ** 32, c >> 32, sub % 2 ** 32, sub >> 32]], dtype=np.uint64)
+        key = np.array([[sd % 2 ** 32, sd >> 32]], dtype=np.uint64)
+        assert np.array_equal(orc.philox4x32(ctr, key)[0], w), (sd, sub, c)
 
 
-def check_uniforms_from_numpy_words(orc):
-    # element i of row b: 21-bit field of word (i // 3) % 4 of the block at counter
-    # (i // 12, b, offset, 0), key (seed, 0): bits 63..43, 42..22 or 21..1 for i % 3 = 0, 1, 2;
-    # u = (field + 1/2) / 2^21. Blocks j >= 1 are compared (numpy cannot start below counter 0).
-    seed, offset, rows, vocab = 123456789, 7, 3, 61
+def check_uniforms_from_reference_words(orc):
+    # element i of row b: field i % 6 of the block at counter (i // 6, b, offset lo, offset hi), key
+    # (seed lo, seed hi); fields 0..2 are bits 63..43, 42..22, 21..1 of w1 * 2^32 + w0, fields 3..5 the
+    # same bits of w3 * 2^32 + w2; u = (field + 1/2) / 2^21
+    seed, offset, rows, vocab = 0x0123456789ABCDEF, 2 ** 40 + 7, 3, 61
     u = orc.uniforms(rows, vocab, seed, offset)
     assert u.shape == (rows, vocab)
+    nblk = -(-vocab // 6)
     for b in range(rows):
-        for i in range(12, vocab):
-            w = int(_numpy_block([i // 12, b, offset, 0], [seed, 0])[(i // 3) % 4])
-            field = (w >> (43 - 21 * (i % 3))) % (1 << 21)
+        # the engine's counter (c lo, c hi, sub lo, sub hi) = (j, b, offset lo, offset hi): c = j + 2^32 b
+        words = reference_blocks([(seed, offset, j + (b << 32)) for j in range(nblk)])
+        for i in range(vocab):
+            w = words[i // 6]
+            x = int(w[1]) << 32 | int(w[0]) if (i % 6) < 3 else int(w[3]) << 32 | int(w[2])
+            field = (x >> (43 - 21 * (i % 3))) % (1 << 21)
             assert u[b, i] == (field + 0.5) / 2.0 ** 21, (b, i)
     assert np.all(u > 0) and np.all(u < 1)
     assert np.array_equal(u.astype(np.float32).astype(np.float64), u)  # exact in fp32
@@ -84,6 +113,6 @@ def check_reproducible_and_distinct_streams(orc):
     assert not np.array_equal(a[0], a[1])                      # another row
 
 
-ALL_CHECKS = [check_philox_matches_numpy, check_uniforms_from_numpy_words, check_literal_definition,
+ALL_CHECKS = [check_philox_matches_rocrand, check_uniforms_from_reference_words, check_literal_definition,
               check_frequencies_follow_softmax, check_dominant_logit_and_small_temperature,
               check_reproducible_and_distinct_streams]
