@@ -18,6 +18,8 @@ One step is one pass of the whole path over seeded synthetic batches:
                    sequences over a 151936-token vocabulary (fp32 logits).
 After the timed steps (outside them): the decode legs as two separate calls,
 the prefill legs as one fused store + prefill call against the separate pair,
+the varlen batch's store beside torch's index_copy_ scatter and a contiguous
+copy of the same bytes,
 host timings of the C++ block manager, the wall-clock decode-step latency eager
 vs graph-captured at batch 1, 16 and 256, and the fp64 oracle timed on the
 host's cores over the decode, prefill, prefix and long-decode batches.
@@ -116,9 +118,27 @@ def separate_decode_leg(pa, torch, b, wl, scale, max_len, ws, out, steps, warmup
             "decode_GBs": round(decode_bytes(wl)["total"] / (dt * 1e-3) / 1e9, 1)}
 
 
-def fused_store_prefill(pa, torch, scale, b3, wl3, b4, wl4, out3, out4, steps, warmup):
+def back_to_back_us(torch, fn, reps=10, rounds=7, warmup=2):
+    """Median over `rounds` of the mean time per call of `reps` back-to-back calls between two events on
+    the current stream: the GPU stays busy, so host launch costs between calls are hidden as in a step."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    per = []
+    for _ in range(rounds):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        per.append(e0.elapsed_time(e1) * 1e3 / reps)
+    return float(np.median(per))
+
+
+def fused_store_prefill(pa, torch, scale, b3, wl3, b4, wl4, out3, out4):
     """The two prefill legs as one pa_store_prefill_varlen call against pa_store_kvcache + pa_prefill_varlen
-    (medians of event-timed calls, alternating, back to back as in the step)."""
+    (time per call of back-to-back calls, the two forms alternating)."""
     legs = {
         "varlen": (lambda: (pa.pa_store_kvcache(b3.k_new, b3.v_new, b3.k_cache, b3.v_cache, b3.slot_mapping),
                             pa.pa_prefill_varlen(b3.q, b3.k_new, b3.v_new, b3.cu_seqlens_q, b3.cu_seqlens_k,
@@ -138,17 +158,39 @@ def fused_store_prefill(pa, torch, scale, b3, wl3, b4, wl4, out3, out4, steps, w
     res = {}
     for name, (unfused, fused) in legs.items():
         t = {"unfused": [], "fused": []}
-        for i in range(warmup + steps):
-            for key, fn in (("unfused", unfused), ("fused", fused)):
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record()
-                fn()
-                e1.record()
-                torch.cuda.synchronize()
-                if i >= warmup:
-                    t[key].append(e0.elapsed_time(e1) * 1e3)
+        for i in range(3):  # alternate the two forms
+            t["unfused"].append(back_to_back_us(torch, unfused))
+            t["fused"].append(back_to_back_us(torch, fused))
         res[name] = {"store_then_prefill_us": round(float(np.median(t["unfused"])), 2),
                      "fused_us": round(float(np.median(t["fused"])), 2)}
+    return res
+
+
+def store_references(pa, torch, b3, wl3):
+    """The varlen batch's store (15.8k tokens, 130 MB moved) beside two references over the same bytes: the
+    same scatter done by torch (index_copy_ of the K rows and of the V rows into the caches by slot), and
+    a plain contiguous device copy of the same byte count (no indirection, no stride). Time per call of
+    back-to-back calls, the three alternating."""
+    hkv, d = wl3.num_kv_heads, wl3.head_dim
+    slots = b3.slot_mapping.long()
+    kflat, vflat = b3.k_cache.view(-1, hkv, d), b3.v_cache.view(-1, hkv, d)
+    src = torch.empty((wl3.num_tokens, 2 * hkv * d), dtype=torch.bfloat16, device=b3.q.device)
+    dst = torch.empty_like(src)
+    calls = {
+        "pa_store_kvcache": lambda: pa.pa_store_kvcache(b3.k_new, b3.v_new, b3.k_cache, b3.v_cache, b3.slot_mapping),
+        "torch_index_copy": lambda: (kflat.index_copy_(0, slots, b3.k_new), vflat.index_copy_(0, slots, b3.v_new)),
+        "contiguous_copy": lambda: dst.copy_(src),
+    }
+    t = {k: [] for k in calls}
+    for i in range(3):  # alternate the three
+        for k, fn in calls.items():
+            t[k].append(back_to_back_us(torch, fn))
+    nbytes = store_bytes(wl3, wl3.num_tokens)
+    res = {k: {"us": round(float(np.median(v)), 2), "GBs": round(nbytes / (float(np.median(v)) * 1e-6) / 1e9, 1)}
+           for k, v in t.items()}
+    res["bytes"] = nbytes
+    res["speedup_vs_torch"] = round(res["torch_index_copy"]["us"] / res["pa_store_kvcache"]["us"], 2)
+    del src, dst
     return res
 
 
@@ -697,8 +739,8 @@ def run(args, pool, n_cores) -> dict:
         if b5 is not None:
             result["long_decode_separate_calls"] = separate_decode_leg(
                 pa, torch, b5, wl5, scale, wl5.max_context_len, ws5, out5, args.steps, args.warmup, args.split_waves)
-        result["store_prefill_fused"] = fused_store_prefill(pa, torch, scale, b3, wl3, b4, wl4, out3, out4,
-                                                            args.steps, args.warmup)
+        result["store_references"] = store_references(pa, torch, b3, wl3)
+        result["store_prefill_fused"] = fused_store_prefill(pa, torch, scale, b3, wl3, b4, wl4, out3, out4)
         result["host_block_manager"] = host_block_manager(wl2, wl4)
         result["decode_graph"] = decode_graph_latency(pa, torch, b2, wl2, scale)
     if pool is not None:

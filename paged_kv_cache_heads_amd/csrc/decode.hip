@@ -512,6 +512,35 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(G >= 8 ? 1 :
   }
 }
 
+// Adds pieces i0 .. i0 + P - 1 (those below n) of the current batch to the
+// running output: lane l of the batch holds piece l's slot and weights f.
+// Piece indexes past n are clamped to n - 1 (a valid slot) and get weight 0.
+template <int G, int P>
+__device__ __forceinline__ void add_pieces(const DecodeArgs& a, int64_t slot, const float (&f)[G], int i0, int n,
+                                           int lane, float (&o0)[G], float (&o1)[G]) {
+  float2 ov[P][G];
+  float fq[P][G];
+#pragma unroll
+  for (int q = 0; q < P; ++q) {
+    const int i = min(i0 + q, n - 1);
+    const int64_t si = __shfl(slot, i);
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      fq[q][j] = i0 + q < n ? __shfl(f[j], i) : 0.f;
+      ov[q][j] = reinterpret_cast<const float2*>(a.ws_o + (si * G + j) * kD)[lane];
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < P; ++q)
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      if (fq[q][j] != 0.f) {
+        o0[j] += fq[q][j] * ov[q][j].x;
+        o1[j] += fq[q][j] * ov[q][j].y;
+      }
+    }
+}
+
 // One wave per (sequence, kv head): zero rows for an empty context, and for
 // a pair cut by share boundaries, combine the pieces its waves left in their
 // slots (slot 1 of the first wave, slot 0 of every later non-empty wave).
@@ -597,33 +626,13 @@ __global__ __launch_bounds__(64) void decode_finalize_kernel(DecodeArgs a) {
       o1[j] *= alpha;
       M[j] = mnew;
     }
-    // the pieces' rows, PR pieces' loads in flight at a time (64 registers of
-    // loads whatever G), added in wave order (a piece with weight 0 is
-    // skipped; its slot may hold stale bits)
+    // the pieces' rows, added in wave order (a piece with weight 0 is skipped;
+    // its slot may hold stale bits): PR pieces' loads in flight at a time (64
+    // registers of loads whatever G) while that many remain, then 4 at a time
     constexpr int PR = G <= 2 ? 16 : 32 / G;
-    for (int i0 = 0; i0 < n; i0 += PR) {
-      float2 ov[PR][G];
-      float fq[PR][G];
-#pragma unroll
-      for (int q = 0; q < PR; ++q) {
-        const int i = min(i0 + q, n - 1);
-        const int64_t si = __shfl(slot, i);
-#pragma unroll
-        for (int j = 0; j < G; ++j) {
-          fq[q][j] = i0 + q < n ? __shfl(f[j], i) : 0.f;
-          ov[q][j] = reinterpret_cast<const float2*>(a.ws_o + (si * G + j) * kD)[lane];
-        }
-      }
-#pragma unroll
-      for (int q = 0; q < PR; ++q)
-#pragma unroll
-        for (int j = 0; j < G; ++j) {
-          if (fq[q][j] != 0.f) {
-            o0[j] += fq[q][j] * ov[q][j].x;
-            o1[j] += fq[q][j] * ov[q][j].y;
-          }
-        }
-    }
+    int i0 = 0;
+    for (; i0 + PR <= n; i0 += PR) add_pieces<G, PR>(a, slot, f, i0, n, lane, o0, o1);
+    for (; i0 < n; i0 += 4) add_pieces<G, 4>(a, slot, f, i0, n, lane, o0, o1);
   }
 #pragma unroll
   for (int j = 0; j < G; ++j) {
