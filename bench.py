@@ -57,6 +57,67 @@ PAGES_END_TO_END = {"value": 1434, "unit": "tok/s", "model": "Qwen3-0.6B", "sequ
                     "in 93.41 s; context only, not comparable with this path's kernel metric"}
 
 
+# ----------------------------------------------------------------------------- timing events
+#
+# Kernel times come from HIP events recorded on the launch stream. torch's events carry a system-scope
+# fence (an L2 writeback and invalidate) that costs about 1.5 us of GPU time per event span, 6% of a
+# 25 us store launch; the HIP runtime documents hipEventDisableSystemFence for such timing. These events
+# are created through the HIP runtime that torch itself has loaded (found in the process map, so that the
+# events and torch's streams belong to one runtime) and are used only for timestamps.
+
+_HIP = None
+_HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
+
+
+def _hip_runtime():
+    global _HIP
+    if _HIP is None:
+        import ctypes
+        path = next((ln.split()[-1] for ln in open("/proc/self/maps") if ln.rstrip().endswith("libamdhip64.so")
+                     or "libamdhip64.so." in ln), None)
+        if path is None:
+            raise RuntimeError("the HIP runtime is not loaded in this process")
+        lib = ctypes.CDLL(path)
+        lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        _HIP = lib
+    return _HIP
+
+
+class TimingEvent:
+    """A HIP timing event without the system-scope fence, with torch.cuda.Event's record() /
+    elapsed_time() interface (milliseconds), recorded on torch's current stream."""
+
+    def __init__(self):
+        import ctypes
+        self._ctypes = ctypes
+        self._hip = _hip_runtime()
+        self._e = ctypes.c_void_p()
+        rc = self._hip.hipEventCreateWithFlags(ctypes.byref(self._e), _HIP_EVENT_DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+
+    def record(self):
+        import torch
+        rc = self._hip.hipEventRecord(self._e, self._ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_time(self, end) -> float:
+        ms = self._ctypes.c_float()
+        rc = self._hip.hipEventElapsedTime(self._ctypes.byref(ms), self._e, end._e)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(ms.value)
+
+    def __del__(self):
+        if getattr(self, "_e", None) is not None and self._e.value:
+            self._hip.hipEventDestroy(self._e)
+            self._e = None
+
+
 def decode_bytes(wl) -> dict:
     """Algorithmic bytes of one decode launch: every context token's K and V row
     of the kv heads, plus q in, out, the used table entries and the lengths."""
@@ -106,7 +167,7 @@ def separate_decode_leg(pa, torch, b, wl, scale, max_len, ws, out, steps, warmup
     for _ in range(warmup):
         once()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    evs = [[TimingEvent() for _ in range(3)] for _ in range(steps)]
     for e in evs:
         once(e)
     torch.cuda.synchronize()
@@ -126,7 +187,7 @@ def back_to_back_us(torch, fn, reps=10, rounds=7, warmup=2):
     torch.cuda.synchronize()
     per = []
     for _ in range(rounds):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0, e1 = TimingEvent(), TimingEvent()
         e0.record()
         for _ in range(reps):
             fn()
@@ -204,7 +265,7 @@ def measured_peaks(torch, dev):
         torch.cuda.synchronize()
         best = float("inf")
         for _ in range(reps):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a, b = TimingEvent(), TimingEvent()
             a.record()
             fn()
             b.record()
@@ -356,7 +417,7 @@ def cold_launches(torch, dev, kernels, calls, reps=10):
         t = []
         for r in range(reps + 2):
             flush.fill_(r & 0xFF)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0, e1 = TimingEvent(), TimingEvent()
             e0.record()
             calls[name]()
             e1.record()
@@ -630,7 +691,7 @@ def run(args, pool, n_cores) -> dict:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in kernels]
+    ev = [[(TimingEvent(), TimingEvent()) for _ in kernels]
           for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
