@@ -228,19 +228,24 @@ def fused_store_prefill(pa, torch, scale, b3, wl3, b4, wl4, out3, out4):
 
 
 def store_references(pa, torch, b3, wl3):
-    """The varlen batch's store (15.8k tokens, 130 MB moved) beside two references over the same bytes: the
-    same scatter done by torch (index_copy_ of the K rows and of the V rows into the caches by slot), and
-    a plain contiguous device copy of the same byte count (no indirection, no stride). Time per call of
-    back-to-back calls, the three alternating."""
+    """The varlen batch's store (15.8k tokens, 130 MB moved) beside references over the same bytes: the
+    same scatter done by torch (index_copy_ of the K rows and of the V rows into the caches by slot), a
+    plain contiguous device copy of the same byte count (no indirection, no stride), and torch copying the
+    store's own source rows (K and V of each token, 4 KiB at the fused projection's 8 KiB row stride) into
+    contiguous memory: the same reads, contiguous writes. Time per call of back-to-back calls, the four
+    alternating."""
     hkv, d = wl3.num_kv_heads, wl3.head_dim
     slots = b3.slot_mapping.long()
     kflat, vflat = b3.k_cache.view(-1, hkv, d), b3.v_cache.view(-1, hkv, d)
     src = torch.empty((wl3.num_tokens, 2 * hkv * d), dtype=torch.bfloat16, device=b3.q.device)
     dst = torch.empty_like(src)
+    # the store's own source rows: each token's K and V, 4 KiB of every fused-projection row
+    kv_rows = b3.qkv[:, wl3.num_q_heads * d:]
     calls = {
         "pa_store_kvcache": lambda: pa.pa_store_kvcache(b3.k_new, b3.v_new, b3.k_cache, b3.v_cache, b3.slot_mapping),
         "torch_index_copy": lambda: (kflat.index_copy_(0, slots, b3.k_new), vflat.index_copy_(0, slots, b3.v_new)),
         "contiguous_copy": lambda: dst.copy_(src),
+        "strided_source_copy": lambda: dst.copy_(kv_rows),
     }
     t = {k: [] for k in calls}
     for i in range(3):  # alternate the three
