@@ -722,18 +722,25 @@ def run(args, pool, n_cores) -> dict:
     # skipped in profiling runs, whose per-kernel statistics cover the timed steps only
     cold = None if args.step_only else cold_launches(torch, dev, kernels, calls)
 
+    # Each roofline also gives the launch's cold figure (run alone right after a 512 MiB write has flushed
+    # L2 and MALL), the timing the protocol asks for where the working set fits in those caches.
+    def cold_fields(leg: str, work: float, peak: float) -> dict:
+        if not cold:
+            return {}
+        return {"cold_launch_us": cold[leg], "frac_cold": round(work / (cold[leg] * 1e-6) / peak, 4)}
+
     def hbm_roofline(kernel: str, leg: str, nbytes: int, traffic=None, **extra):
         gbs = nbytes / (ms[leg] * 1e-3) / 1e9
         return {"bound": "hbm", "kernel": kernel, "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic, "bytes_per_launch": nbytes,
-                "avg_launch_us": round(ms[leg] * 1e3, 2), **extra}
+                "avg_launch_us": round(ms[leg] * 1e3, 2), **cold_fields(leg, nbytes / 1e9, HBM_PEAK_GBS), **extra}
 
     def mfma_roofline(kernel: str, leg: str, flops: int):
         tf = flops / (ms[leg] * 1e-3) / 1e12
         return {"bound": "mfma", "kernel": kernel, "achieved": round(tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
                 "frac_of_measured_gemm": round(tf / peaks["bf16_gemm_TFLOPs"], 4), "flops_per_launch": flops,
-                "avg_launch_us": round(ms[leg] * 1e3, 2)}
+                "avg_launch_us": round(ms[leg] * 1e3, 2), **cold_fields(leg, flops / 1e12, MFMA_BF16_PEAK_TFLOPS)}
 
     dbytes = decode_bytes(wl2)
     leg_bytes = dbytes["total"] + store_bytes(wl2, wl2.num_seqs)  # the decode plus the new tokens' store

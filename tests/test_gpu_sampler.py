@@ -100,3 +100,42 @@ def test_sampler_special_rows_and_streams(dev):
     assert np.array_equal(a, _run(wide, np.ones(64), 8, 1, dev))
     b = _run(wide, np.ones(64), 8, 2, dev)
     assert (a != b).sum() > 32
+
+
+def _run_strided(logits, temps, seed, offset, dev, pad):
+    """logits [B, V] as the first V columns of a [B, V + pad] device tensor (rows V + pad elements apart)."""
+    b, v = logits.shape
+    wide = np.full((b, v + pad), 7.0, dtype=np.float32)  # the padding would win if it were read
+    wide[:, :v] = logits
+    lg = torch.as_tensor(wide).to(dev)[:, :v]
+    assert lg.stride(0) == v + pad
+    out = pa.pa_sample_gumbel(lg, torch.as_tensor(np.asarray(temps, np.float32)).to(dev), seed, offset)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.int64)
+
+
+@pytest.mark.parametrize("vocab,pad", [(12288, 4), (12288, 3), (20000, 8), (20000, 1)])
+def test_sampler_strided_rows(dev, vocab, pad):
+    # rows 16-byte aligned (pad a multiple of 4: vector loads) or not (single loads), padding never read
+    announce(f"sampler strided rows vocab {vocab} pad {pad}")
+    rng = np.random.default_rng(vocab + pad)
+    logits = (rng.standard_normal((6, vocab)) * 2).astype(np.float32)
+    temps = rng.uniform(0.5, 1.5, 6).astype(np.float32)
+    got = _run_strided(logits, temps, 31, pad, dev, pad)
+    assert np.all((got >= 0) & (got < vocab))
+    _check(got, logits.astype(np.float64), temps, 31, pad)
+
+
+def test_sampler_ties_across_layouts(dev):
+    # +inf logits tie exactly: the lowest index must win wherever the tied elements sit (the same group of
+    # three, neighbouring lanes, the end of one wave's 768-logit span and the start of the next, the
+    # vector-loaded part against the row's ragged end)
+    announce("sampler ties")
+    vocab = 20000
+    cases = [[9, 10, 11], [10, 11], [11, 12], [767, 768], [766, 1535, 1536], [12287, 12288],
+             [18433, 19999], [19998, 19999], [5, 19999]]
+    lg = np.random.default_rng(11).standard_normal((len(cases), vocab))
+    for r, idx in enumerate(cases):
+        lg[r, idx] = np.inf
+    got = _run(lg, np.ones(len(cases)), 3, 4, dev)
+    assert got.tolist() == [min(c) for c in cases]
