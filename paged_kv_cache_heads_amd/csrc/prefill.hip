@@ -432,9 +432,11 @@ void prefill_kernel(PrefillArgs a) {
       mx = max_xor32(mx);
       if (__ballot(mx > m[u] + tau)) {
         const float mnew = fmaxf(m[u], mx);
-        const float alpha = fast_exp2((m[u] - mnew) * c);
+        if (tile != 0) {  // on the first tile the accumulators are still zero
+          const float alpha = fast_exp2((m[u] - mnew) * c);
 #pragma unroll
-        for (int dt = 0; dt < 9; ++dt) oacc[u][dt] *= alpha;
+          for (int dt = 0; dt < 9; ++dt) oacc[u][dt] *= alpha;
+        }
         m[u] = mnew;
       }
       const float mc = m[u] * c;
