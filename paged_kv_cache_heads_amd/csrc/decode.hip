@@ -41,6 +41,7 @@
 #include <math.h>
 
 #include <mutex>
+#include <type_traits>
 
 #include "../../include/pa.h"
 #include "common.h"
@@ -95,10 +96,14 @@ __device__ __forceinline__ float group8_reduce(const float (&v)[TPL], int s) {
     }
     float c = (b1 ? a[1] : a[0]) + dpp<kDppXor2>(b1 ? a[0] : a[1]);
     return c + dpp<kDppXor1>(c);
-  } else {
-    static_assert(TPL == 2, "2 or 4 tokens per lane");
+  } else if constexpr (TPL == 2) {
     const bool b2 = s & 4;
     float c = (b2 ? v[1] : v[0]) + dpp<kDppHalfMirror>(b2 ? v[0] : v[1]);
+    c += dpp<kDppXor2>(c);
+    return c + dpp<kDppXor1>(c);
+  } else {
+    static_assert(TPL == 1, "1, 2 or 4 tokens per lane");
+    float c = v[0] + dpp<kDppHalfMirror>(v[0]);
     c += dpp<kDppXor2>(c);
     return c + dpp<kDppXor1>(c);
   }
@@ -199,13 +204,27 @@ struct DecodeState {
   float m[G], l[G], acc[G][16];
 };
 
+// The pair's query, dims 8s..8s+7 (lo) and 64+8s..64+8s+7 (hi) of each of the
+// G heads for the lane's s. G <= 4: held in registers.
 template <int G>
 struct QRegs {
   uint4 lo[G], hi[G];
+  __device__ __forceinline__ uint4 get_lo(int j) const { return lo[j]; }
+  __device__ __forceinline__ uint4 get_hi(int j) const { return hi[j]; }
 };
 
-template <int G, int TPL>
-__device__ __forceinline__ void compute_chunk(DecodeState<G>& st, const QRegs<G>& q, const ChunkRegs<TPL>& c,
+// G = 8: the 128 accumulators per lane leave no room for 64 query registers
+// at two waves per SIMD, so the query lives in the wave's 2 KiB of LDS and
+// each head's two 16-byte pieces are read when that head is scored.
+struct QLds {
+  uint4* base;  // [8 heads][lo, hi][8 lanes s]
+  int s;
+  __device__ __forceinline__ uint4 get_lo(int j) const { return base[(2 * j) * 8 + s]; }
+  __device__ __forceinline__ uint4 get_hi(int j) const { return base[(2 * j + 1) * 8 + s]; }
+};
+
+template <int G, int TPL, class QS>
+__device__ __forceinline__ void compute_chunk(DecodeState<G>& st, const QS& q, const ChunkRegs<TPL>& c,
                                               int nvalid, float scale_log2e, int lane, int r, int s) {
   constexpr int kDup = 8 / TPL;  // lanes holding each token's score
   const bool valid = ((s / kDup) * 8 + r) < nvalid;
@@ -213,17 +232,18 @@ __device__ __forceinline__ void compute_chunk(DecodeState<G>& st, const QRegs<G>
 #pragma unroll
   for (int j = 0; j < G; ++j) {
     float sc[TPL];
+    const uint4 qlo = q.get_lo(j), qhi = q.get_hi(j);
 #pragma unroll
     for (int i = 0; i < TPL; ++i) {
       float d = 0.f;
-      d = dot2_bf16(q.lo[j].x, c.k[i][0].x, d);
-      d = dot2_bf16(q.lo[j].y, c.k[i][0].y, d);
-      d = dot2_bf16(q.lo[j].z, c.k[i][0].z, d);
-      d = dot2_bf16(q.lo[j].w, c.k[i][0].w, d);
-      d = dot2_bf16(q.hi[j].x, c.k[i][1].x, d);
-      d = dot2_bf16(q.hi[j].y, c.k[i][1].y, d);
-      d = dot2_bf16(q.hi[j].z, c.k[i][1].z, d);
-      d = dot2_bf16(q.hi[j].w, c.k[i][1].w, d);
+      d = dot2_bf16(qlo.x, c.k[i][0].x, d);
+      d = dot2_bf16(qlo.y, c.k[i][0].y, d);
+      d = dot2_bf16(qlo.z, c.k[i][0].z, d);
+      d = dot2_bf16(qlo.w, c.k[i][0].w, d);
+      d = dot2_bf16(qhi.x, c.k[i][1].x, d);
+      d = dot2_bf16(qhi.y, c.k[i][1].y, d);
+      d = dot2_bf16(qhi.z, c.k[i][1].z, d);
+      d = dot2_bf16(qhi.w, c.k[i][1].w, d);
       sc[i] = d;
     }
     float x = group8_reduce<TPL>(sc, s);  // score of token (s / kDup) * 8 + r
@@ -301,6 +321,24 @@ __device__ __forceinline__ void load_q(QRegs<G>& q, const DecodeArgs& a, int b, 
     q.lo[j] = load16(qp + 8 * s);
     q.hi[j] = load16(qp + 64 + 8 * s);
   }
+}
+
+// G = 8: lane (j, s) = (lane / 8, lane % 8) loads head j's two pieces for s
+// and stores them to the wave's LDS query. Every read of the previous pair's
+// query precedes these writes in the wave's program order, and LDS operations
+// of one wave complete in order; the fences keep the compiler from moving
+// accesses across them.
+__device__ __forceinline__ void load_q(QLds& q, const DecodeArgs& a, int b, int g, int lane) {
+  const int j = lane >> 3, s8 = lane & 7;
+  const bf16_t* qp = a.q + (int64_t)b * a.q_seq_stride + (int64_t)(g * 8 + j) * kD;
+  const uint4 lo = load16(qp + 8 * s8), hi = load16(qp + 64 + 8 * s8);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  q.base[(2 * j) * 8 + s8] = lo;
+  q.base[(2 * j + 1) * 8 + s8] = hi;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 // Next chunk in (sequence, kv head, chunk) order; skips empty sequences.
@@ -383,7 +421,7 @@ __device__ __forceinline__ void finish_piece(const DecodeState<G>& st, const Dec
 }
 
 template <int G, int TPL>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(G >= 8 ? 1 : 2, 8))) void decode_split_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void decode_split_kernel(DecodeArgs a) {
   constexpr int CH = 8 * TPL;  // tokens per chunk
   const int wave = blockIdx.x, lane = threadIdx.x;
   const int r = lane >> 3, s = lane & 7;
@@ -457,10 +495,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(G >= 8 ? 1 :
   const uint32_t row_bytes = (uint32_t)a.num_kv_heads * kD * 2;
   const uint32_t lane_off = r * row_bytes + 16 * s;
   ChunkRegs<TPL> c0, c1;
-  QRegs<G> q;
+  __shared__ uint4 q_lds[G == 8 ? 128 : 1];
+  typename std::conditional<G == 8, QLds, QRegs<G>>::type q;
+  if constexpr (G == 8) q = QLds{q_lds, s};
+  const int qsel = G == 8 ? lane : s;  // load_q's lane argument
   DecodeState<G> st;
   load_chunk(c0, a, cur, row_bytes, lane_off, r, s);
-  load_q(q, a, cur.b, cur.g, s);
+  load_q(q, a, cur.b, cur.g, qsel);
   reset_state(st);
   int k0 = cur.k;  // first chunk of the current piece
   const float sc = a.scale_log2e;
@@ -484,7 +525,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(G >= 8 ? 1 :
         if (!more) break;
         reset_state(st);
         k0 = 0;
-        load_q(q, a, nxt.b, nxt.g, s);
+        load_q(q, a, nxt.b, nxt.g, qsel);
       }
       cur = nxt;
       ++c;
@@ -504,7 +545,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(G >= 8 ? 1 :
         if (!more) break;
         reset_state(st);
         k0 = 0;
-        load_q(q, a, nxt.b, nxt.g, s);
+        load_q(q, a, nxt.b, nxt.g, qsel);
       }
       cur = nxt;
       ++c;
@@ -642,11 +683,11 @@ __global__ __launch_bounds__(64) void decode_finalize_kernel(DecodeArgs a) {
   }
 }
 
-// Tokens per lane per chunk: 4 while the G heads' state is small, else 2, so
-// that two waves fit per SIMD.
+// Tokens per lane per chunk: 4 while the G heads' state is small, 2 at G = 4
+// and 1 at G = 8 (128 accumulators per lane), so that two waves fit per SIMD.
 template <int G>
 static hipError_t launch_decode_g(const DecodeArgs& a, hipStream_t stream) {
-  constexpr int TPL = G <= 2 ? 4 : 2;
+  constexpr int TPL = G <= 2 ? 4 : (G <= 4 ? 2 : 1);
   decode_split_kernel<G, TPL><<<dim3(a.num_waves), dim3(64), 0, stream>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -654,7 +695,7 @@ static hipError_t launch_decode_g(const DecodeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-int decode_chunk_tokens(int group) { return group <= 2 ? 32 : 16; }
+int decode_chunk_tokens(int group) { return group <= 2 ? 32 : (group <= 4 ? 16 : 8); }
 
 hipError_t launch_decode(const DecodeArgs& a, int group, hipStream_t stream) {
   if (a.num_seqs == 0) return hipSuccess;
