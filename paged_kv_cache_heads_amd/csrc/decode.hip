@@ -9,7 +9,8 @@
 // (page "nano-vLLM 最小化vLLM重新实现", section 5 "注意力机制": decode attention
 // over the paged KV cache; section 3 "块管理器": fixed-size blocks).
 //
-// Design for gfx950 (HBM-bound, no MFMA):
+// Design for gfx950 (HBM-bound; vector arithmetic for 1, 2 and 4 query heads
+// per kv head, the matrix cores at 8, see decode_mfma_kernel):
 // * Work is split stream-K style. The (sequence, kv head) pairs are laid end
 //   to end as runs of chunks of 8*TPL tokens, and each of `num_waves`
 //   one-wave workgroups takes an equal share of that chunk sequence, so all
@@ -41,11 +42,11 @@
 #include <math.h>
 
 #include <mutex>
-#include <type_traits>
 
 #include "../../include/pa.h"
 #include "common.h"
 #include "launch.h"
+#include "mfma_tiles.h"
 
 namespace pa {
 
@@ -96,14 +97,10 @@ __device__ __forceinline__ float group8_reduce(const float (&v)[TPL], int s) {
     }
     float c = (b1 ? a[1] : a[0]) + dpp<kDppXor2>(b1 ? a[0] : a[1]);
     return c + dpp<kDppXor1>(c);
-  } else if constexpr (TPL == 2) {
+  } else {
+    static_assert(TPL == 2, "2 or 4 tokens per lane");
     const bool b2 = s & 4;
     float c = (b2 ? v[1] : v[0]) + dpp<kDppHalfMirror>(b2 ? v[0] : v[1]);
-    c += dpp<kDppXor2>(c);
-    return c + dpp<kDppXor1>(c);
-  } else {
-    static_assert(TPL == 1, "1, 2 or 4 tokens per lane");
-    float c = v[0] + dpp<kDppHalfMirror>(v[0]);
     c += dpp<kDppXor2>(c);
     return c + dpp<kDppXor1>(c);
   }
@@ -205,7 +202,7 @@ struct DecodeState {
 };
 
 // The pair's query, dims 8s..8s+7 (lo) and 64+8s..64+8s+7 (hi) of each of the
-// G heads for the lane's s. G <= 4: held in registers.
+// G heads for the lane's s.
 template <int G>
 struct QRegs {
   uint4 lo[G], hi[G];
@@ -213,18 +210,8 @@ struct QRegs {
   __device__ __forceinline__ uint4 get_hi(int j) const { return hi[j]; }
 };
 
-// G = 8: the 128 accumulators per lane leave no room for 64 query registers
-// at two waves per SIMD, so the query lives in the wave's 2 KiB of LDS and
-// each head's two 16-byte pieces are read when that head is scored.
-struct QLds {
-  uint4* base;  // [8 heads][lo, hi][8 lanes s]
-  int s;
-  __device__ __forceinline__ uint4 get_lo(int j) const { return base[(2 * j) * 8 + s]; }
-  __device__ __forceinline__ uint4 get_hi(int j) const { return base[(2 * j + 1) * 8 + s]; }
-};
-
-template <int G, int TPL, class QS>
-__device__ __forceinline__ void compute_chunk(DecodeState<G>& st, const QS& q, const ChunkRegs<TPL>& c,
+template <int G, int TPL>
+__device__ __forceinline__ void compute_chunk(DecodeState<G>& st, const QRegs<G>& q, const ChunkRegs<TPL>& c,
                                               int nvalid, float scale_log2e, int lane, int r, int s) {
   constexpr int kDup = 8 / TPL;  // lanes holding each token's score
   const bool valid = ((s / kDup) * 8 + r) < nvalid;
@@ -323,24 +310,6 @@ __device__ __forceinline__ void load_q(QRegs<G>& q, const DecodeArgs& a, int b, 
   }
 }
 
-// G = 8: lane (j, s) = (lane / 8, lane % 8) loads head j's two pieces for s
-// and stores them to the wave's LDS query. Every read of the previous pair's
-// query precedes these writes in the wave's program order, and LDS operations
-// of one wave complete in order; the fences keep the compiler from moving
-// accesses across them.
-__device__ __forceinline__ void load_q(QLds& q, const DecodeArgs& a, int b, int g, int lane) {
-  const int j = lane >> 3, s8 = lane & 7;
-  const bf16_t* qp = a.q + (int64_t)b * a.q_seq_stride + (int64_t)(g * 8 + j) * kD;
-  const uint4 lo = load16(qp + 8 * s8), hi = load16(qp + 64 + 8 * s8);
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  q.base[(2 * j) * 8 + s8] = lo;
-  q.base[(2 * j + 1) * 8 + s8] = hi;
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 // Next chunk in (sequence, kv head, chunk) order; skips empty sequences.
 __device__ __forceinline__ Pos next_pos(const Pos& p, const DecodeArgs& a, int ch, int ns) {
   if (p.k + 1 < p.nc) return Pos{p.b, p.g, p.k + 1, p.len, p.nc};
@@ -420,16 +389,16 @@ __device__ __forceinline__ void finish_piece(const DecodeState<G>& st, const Dec
   }
 }
 
-template <int G, int TPL>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void decode_split_kernel(DecodeArgs a) {
-  constexpr int CH = 8 * TPL;  // tokens per chunk
-  const int wave = blockIdx.x, lane = threadIdx.x;
-  const int r = lane >> 3, s = lane & 7;
+// Wave `wave`'s share [lo, hi) of the chunk sequence (chunks of ch tokens, in
+// (sequence, kv head, chunk) order over the ns live sequences) and the
+// position of its first chunk. False when the share is empty.
+__device__ __forceinline__ bool locate_share(const DecodeArgs& a, int ch, int wave, int lane, int& ns, int64_t& lo,
+                                             int64_t& hi, Pos& cur) {
   const int64_t nw = a.num_waves;
   // the first 256 lengths are loaded once and serve both scans below
   int lu0[4];
   load4_lens(a.context_lens, lane * 4, a.num_seqs, lu0);
-  const int ns = live_seqs(a);
+  ns = live_seqs(a);
   int64_t total = 0;
   for (int base = 0; base < ns; base += 256) {
     int x = 0, lu[4];
@@ -440,15 +409,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
       load4_lens(a.context_lens, base + lane * 4, a.num_seqs, lu);
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) x += base + lane * 4 + u < ns ? chunks_of(lu[u], CH) : 0;
+    for (int u = 0; u < 4; ++u) x += base + lane * 4 + u < ns ? chunks_of(lu[u], ch) : 0;
     total += uniform(wave_sum_i32(x));
   }
   total *= a.num_kv_heads;
-  const int64_t lo = share_begin(wave, total, nw), hi = share_begin(wave + 1, total, nw);
-  if (lo >= hi) return;
+  lo = share_begin(wave, total, nw);
+  hi = share_begin(wave + 1, total, nw);
+  if (lo >= hi) return false;
 
   // locate chunk `lo`: the sequence b with kvh*prefix(b) <= lo < kvh*prefix(b+1)
-  Pos cur{0, 0, 0, 0, 0};
+  cur = Pos{0, 0, 0, 0, 0};
   {
     int64_t run = 0;
     for (int base = 0; base < ns; base += 256) {
@@ -463,7 +433,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
       for (int u = 0; u < 4; ++u) {
         const int b = base + lane * 4 + u;
         len[u] = b < ns ? lu[u] : 0;
-        x[u] = chunks_of(len[u], CH) * a.num_kv_heads;
+        x[u] = chunks_of(len[u], ch) * a.num_kv_heads;
         sum += x[u];
       }
       const int incl = wave_inclusive_scan_i32(sum, lane);
@@ -479,7 +449,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
           if (xu > 0 && lo < beg + xu && cur.nc == 0) {
             cur.b = base + src * 4 + u;
             cur.len = uniform(__shfl(len[u], src));
-            cur.nc = chunks_of(cur.len, CH);
+            cur.nc = chunks_of(cur.len, ch);
             const int64_t rel = lo - beg;
             cur.g = (int)(rel / cur.nc);
             cur.k = (int)(rel % cur.nc);
@@ -492,16 +462,26 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
     }
   }
 
+  return true;
+}
+
+template <int G, int TPL>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void decode_split_kernel(DecodeArgs a) {
+  constexpr int CH = 8 * TPL;  // tokens per chunk
+  const int wave = blockIdx.x, lane = threadIdx.x;
+  const int r = lane >> 3, s = lane & 7;
+  int ns;
+  int64_t lo, hi;
+  Pos cur;
+  if (!locate_share(a, CH, wave, lane, ns, lo, hi, cur)) return;
+
   const uint32_t row_bytes = (uint32_t)a.num_kv_heads * kD * 2;
   const uint32_t lane_off = r * row_bytes + 16 * s;
   ChunkRegs<TPL> c0, c1;
-  __shared__ uint4 q_lds[G == 8 ? 128 : 1];
-  typename std::conditional<G == 8, QLds, QRegs<G>>::type q;
-  if constexpr (G == 8) q = QLds{q_lds, s};
-  const int qsel = G == 8 ? lane : s;  // load_q's lane argument
+  QRegs<G> q;
   DecodeState<G> st;
   load_chunk(c0, a, cur, row_bytes, lane_off, r, s);
-  load_q(q, a, cur.b, cur.g, qsel);
+  load_q(q, a, cur.b, cur.g, s);
   reset_state(st);
   int k0 = cur.k;  // first chunk of the current piece
   const float sc = a.scale_log2e;
@@ -525,7 +505,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
         if (!more) break;
         reset_state(st);
         k0 = 0;
-        load_q(q, a, nxt.b, nxt.g, qsel);
+        load_q(q, a, nxt.b, nxt.g, s);
       }
       cur = nxt;
       ++c;
@@ -545,10 +525,254 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
         if (!more) break;
         reset_state(st);
         k0 = 0;
-        load_q(q, a, nxt.b, nxt.g, qsel);
+        load_q(q, a, nxt.b, nxt.g, s);
       }
       cur = nxt;
       ++c;
+    }
+  }
+}
+
+// ---- the split pass on the matrix cores -------------------------------------
+//
+// With G query heads per kv head the decode is a small dense contraction: G
+// query rows against every key of the pair. The kernel above does it with
+// vector dot products, whose cost grows with G until, at G = 8, the vector
+// work rather than HBM sets the time. This kernel runs the same stream-K
+// split (32-token chunks) on the MFMA units, with the G queries as the
+// columns of 16x16x32 bf16 tiles (columns G..15 are zero and ignored):
+//   Sᵀ (32 keys x 16 queries) = K Qᵀ: K rows straight from global memory into
+//     the A operand (lane (g, c): key c of a 16-key tile, dims 32 ks + 8 g ..
+//     + 7), Qᵀ held in registers;
+//   online softmax in log2 units per query column, rescaled lazily (when a
+//     column's maximum grows by more than 2^8), p in fp32;
+//   Oᵀ (128 dims x 16 queries) += Vᵀ Pᵀ: V staged in LDS by DMA (two 8 KiB
+//     buffers, the next chunk in flight) and read transposed; P is split into
+//     bf16 high and low parts (p = hi + lo to 2^-16) and both are multiplied,
+//     so the weights keep close to fp32 precision; the row sums are the fp32
+//     sums of p.
+// Pieces go to the same workspace slots, in the same (max, sum, output)
+// format, and the same finalize pass combines them.
+template <int G>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void decode_mfma_kernel(DecodeArgs a) {
+  constexpr int CH = 32;  // tokens per chunk
+  static_assert(G <= 16, "the queries of a kv head are the columns of one 16-column tile");
+  __shared__ __attribute__((aligned(1024))) char vbuf0[CH * 256];
+  __shared__ __attribute__((aligned(1024))) char vbuf1[CH * 256];
+  const int wave = blockIdx.x, lane = threadIdx.x;
+  const int g = lane >> 4, col = lane & 15;
+  int ns;
+  int64_t lo, hi;
+  Pos cur;
+  if (!locate_share(a, CH, wave, lane, ns, lo, hi, cur)) return;
+
+  const int64_t row_elems = (int64_t)a.num_kv_heads * kD;  // elements between tokens' rows in the cache
+  // Vᵀ operand reads: lane (g, c) takes dims 16 dt + c of keys 4 g .. 4 g + 3 (low half) and 16 + 4 g .. (high)
+  uint32_t voff[8];
+  {
+    const int trow = 4 * g + (col >> 2), tq = col & 3;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) voff[dt] = v_off(trow, 2 * dt + (tq >> 1)) + (tq & 1) * 8;
+  }
+
+  // Issue the loads of chunk p: K rows into kreg (A operand layout), V rows by
+  // DMA into vbuf (row-major, swizzled). Rows past the context end are read
+  // from the last token (their scores are masked; their V rows must be
+  // finite); the new token (pa_store_decode) comes from k_new / v_new.
+  auto issue = [&](const Pos& p, uint4 (&kreg)[2][4], char* vbuf) {
+    const int tok0 = p.k * CH;
+    const int nvalid = min(CH, p.len - tok0);
+    const int blk = a.block_tables[(int64_t)p.b * a.max_blocks_per_seq + tok0 / a.block_size];
+    const int64_t base = ((int64_t)blk * a.block_size + tok0 % a.block_size) * row_elems + (int64_t)p.g * kD;
+    const bool has_new = a.k_new != nullptr;
+    const int new_row = p.len - 1 - tok0;  // row of the new token in this chunk (if < CH)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int row = min(16 * t + col, nvalid - 1);
+      const uint16_t* kr = (has_new && row == new_row) ? a.k_new + p.b * a.k_new_stride + p.g * kD
+                                                       : a.k_cache + base + row * row_elems;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) kreg[t][ks] = load16_nt(kr + 32 * ks + 8 * g);
+    }
+    // DMA instruction u fills rows 4u .. 4u + 3: lane (g, c) supplies row
+    // 4u + g, physical chunk c, i.e. the logical chunk the V swizzle puts there
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int row = min(4 * u + g, nvalid - 1);
+      const int chunk = col ^ (((4 * u + g) & 7) << 1);
+      const uint16_t* vr = (has_new && row == new_row) ? a.v_new + p.b * a.v_new_stride + p.g * kD
+                                                       : a.v_cache + base + row * row_elems;
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(vr) + 16 * chunk, (lds_void_t*)(vbuf + u * 1024),
+                                       16, 0, 0);
+    }
+  };
+
+  // Qᵀ operand of the pair: query column col (< G), dims 32 ks + 8 g .. + 7
+  uint4 qop[4];
+  auto load_qop = [&](const Pos& p) {
+    const bf16_t* qr = a.q + (int64_t)p.b * a.q_seq_stride + (int64_t)(p.g * G + min(col, G - 1)) * kD;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const uint4 v = load16(qr + 32 * ks + 8 * g);
+      qop[ks] = col < G ? v : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+
+  f32x4_t oacc[8];
+  float m, lsum;
+  bool fresh;
+  auto reset = [&]() {
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) oacc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    m = kNegBig;
+    lsum = 0.f;
+    fresh = true;
+  };
+  const float c = a.scale_log2e;
+  constexpr float tau = 8.f;  // lazy-rescale threshold, log2 units
+
+  // One chunk: scores, softmax, Vᵀ Pᵀ. more: the next chunk's 16 loads are in flight.
+  auto compute = [&](const Pos& p, const uint4 (&kreg)[2][4], const char* vbuf, bool more) {
+    const int nvalid = min(CH, p.len - p.k * CH);
+    f32x4_t sacc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) sacc[t] = mfma16x16x32(kreg[t][ks], qop[ks], sacc[t]);
+    // lane (g, col): query col, keys 16 t + 4 g + i
+    float x[2][4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[t][i] = sacc[t][i] * c;
+    if (nvalid < CH) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[t][i] = 16 * t + 4 * g + i < nvalid ? x[t][i] : -INFINITY;
+    }
+    float mx = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
+                     fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
+    mx = max_xor32(max_xor16(mx));
+    if (__ballot(mx > m + tau)) {
+      const float mnew = fmaxf(m, mx);
+      if (!fresh) {
+        const float alpha = fast_exp2(m - mnew);
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) oacc[dt] *= alpha;
+        lsum *= alpha;
+      }
+      m = mnew;
+    }
+    fresh = false;
+    float pv[2][4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pv[t][i] = fast_exp2(x[t][i] - m);
+        lsum += pv[t][i];
+      }
+    // Pᵀ operand (lane (g, col): query col, keys 4 g .. 4 g + 3 of each 16-key
+    // tile), high and low bf16 parts
+    uint32_t ph[4], pl[4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; i += 2) {
+        const uint32_t h = pack_bf16x2(pv[t][i], pv[t][i + 1]);
+        ph[2 * t + i / 2] = h;
+        pl[2 * t + i / 2] = pack_bf16x2(pv[t][i] - bf16_lo(h), pv[t][i + 1] - bf16_hi(h));
+      }
+    const uint4 poph = make_uint4(ph[0], ph[1], ph[2], ph[3]);
+    const uint4 popl = make_uint4(pl[0], pl[1], pl[2], pl[3]);
+    // the chunk's V DMA has landed once at most the next chunk's 16 loads are outstanding
+    if (more) wait_vmem_le<16>(); else wait_vmem_le<0>();
+    asm volatile("" ::: "memory");
+    typedef __attribute__((address_space(3))) const char lds_char_t;
+    lds_char_t* vl = (lds_char_t*)vbuf;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const s16x4_t l4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vl + voff[dt]));
+      const s16x4_t h4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vl + 16 * 256 + voff[dt]));
+      const v2i_t l2 = __builtin_bit_cast(v2i_t, l4), h2 = __builtin_bit_cast(v2i_t, h4);
+      const uint4 vop = make_uint4(l2.x, l2.y, h2.x, h2.y);
+      oacc[dt] = mfma16x16x32(vop, poph, oacc[dt]);
+      oacc[dt] = mfma16x16x32(vop, popl, oacc[dt]);
+    }
+  };
+
+  // The pair's piece ends: a whole pair goes to the output, a cut one to its
+  // slot (slot 1 of the wave for the piece that starts the pair's cut, slot 0
+  // for the piece at the wave's start).
+  auto finish = [&](const Pos& p, int k0) {
+    const float ls = sum_xor16_32(lsum);
+    const bool whole = (k0 == 0) && (p.k == p.nc - 1);
+    const int64_t slot = (int64_t)wave * 2 + (k0 > 0 ? 0 : 1);
+    if (col < G) {
+      if (whole) {
+        const float inv = 1.f / ls;
+        uint16_t* o = a.out + ((int64_t)p.b * a.num_q_heads + p.g * G + col) * kD + 4 * g;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+          *reinterpret_cast<uint2*>(o + 16 * dt) =
+              make_uint2(pack_bf16x2(oacc[dt][0] * inv, oacc[dt][1] * inv), pack_bf16x2(oacc[dt][2] * inv, oacc[dt][3] * inv));
+      } else {
+        float* o = a.ws_o + (slot * G + col) * kD + 4 * g;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+          *reinterpret_cast<float4*>(o + 16 * dt) = make_float4(oacc[dt][0], oacc[dt][1], oacc[dt][2], oacc[dt][3]);
+        if (g == 0) reinterpret_cast<float2*>(a.ws_ml)[slot * G + col] = make_float2(m, ls);
+      }
+    }
+  };
+
+  uint4 kA[2][4], kB[2][4];
+  issue(cur, kA, vbuf0);
+  load_qop(cur);
+  reset();
+  int k0 = cur.k;  // first chunk of the current piece
+  // two stages with the register sets and LDS buffers swapped
+  for (int64_t ci = lo;;) {
+    {
+      const bool more = ci + 1 < hi;
+      Pos nxt = cur;
+      bool new_pair = false;
+      if (more) {
+        nxt = next_pos(cur, a, CH, ns);
+        new_pair = nxt.b != cur.b || nxt.g != cur.g;
+        issue(nxt, kB, vbuf1);
+      }
+      compute(cur, kA, vbuf0, more);
+      if (!more || new_pair) {
+        finish(cur, k0);
+        if (!more) break;
+        reset();
+        k0 = 0;
+        load_qop(nxt);
+      }
+      cur = nxt;
+      ++ci;
+    }
+    {
+      const bool more = ci + 1 < hi;
+      Pos nxt = cur;
+      bool new_pair = false;
+      if (more) {
+        nxt = next_pos(cur, a, CH, ns);
+        new_pair = nxt.b != cur.b || nxt.g != cur.g;
+        issue(nxt, kA, vbuf0);
+      }
+      compute(cur, kB, vbuf1, more);
+      if (!more || new_pair) {
+        finish(cur, k0);
+        if (!more) break;
+        reset();
+        k0 = 0;
+        load_qop(nxt);
+      }
+      cur = nxt;
+      ++ci;
     }
   }
 }
@@ -683,19 +907,27 @@ __global__ __launch_bounds__(64) void decode_finalize_kernel(DecodeArgs a) {
   }
 }
 
-// Tokens per lane per chunk: 4 while the G heads' state is small, 2 at G = 4
-// and 1 at G = 8 (128 accumulators per lane), so that two waves fit per SIMD.
+// G = 8 takes the split pass on the matrix cores. Same-box timings of the
+// two split passes (config-2 lengths at Hkv = 8; 512 long contexts at G = 4):
+// G = 8 370 us vector, 237 us matrix; G = 4 213 / 224 us and 2286 / 2321 us.
+constexpr int kMfmaMinGroup = 8;
+
+// Vector split pass: tokens per lane per chunk 4 while the G heads' state is
+// small, else 2, so that two waves fit per SIMD. Matrix split pass: 32-token
+// chunks.
 template <int G>
 static hipError_t launch_decode_g(const DecodeArgs& a, hipStream_t stream) {
-  constexpr int TPL = G <= 2 ? 4 : (G <= 4 ? 2 : 1);
-  decode_split_kernel<G, TPL><<<dim3(a.num_waves), dim3(64), 0, stream>>>(a);
+  constexpr bool kMfma = G >= kMfmaMinGroup;
+  constexpr int TPL = (kMfma || G <= 2) ? 4 : 2;  // the finalize pass's chunk: 8 TPL tokens
+  if constexpr (kMfma) decode_mfma_kernel<G><<<dim3(a.num_waves), dim3(64), 0, stream>>>(a);
+  else decode_split_kernel<G, TPL><<<dim3(a.num_waves), dim3(64), 0, stream>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   decode_finalize_kernel<G, TPL><<<dim3(a.num_seqs * a.num_kv_heads), dim3(64), 0, stream>>>(a);
   return hipGetLastError();
 }
 
-int decode_chunk_tokens(int group) { return group <= 2 ? 32 : (group <= 4 ? 16 : 8); }
+int decode_chunk_tokens(int group) { return (group >= kMfmaMinGroup || group <= 2) ? 32 : 16; }
 
 hipError_t launch_decode(const DecodeArgs& a, int group, hipStream_t stream) {
   if (a.num_seqs == 0) return hipSuccess;

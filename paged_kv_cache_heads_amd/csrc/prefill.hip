@@ -54,29 +54,15 @@
 
 #include "common.h"
 #include "launch.h"
+#include "mfma_tiles.h"
 
 namespace pa {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
 constexpr int kPD = 128;        // head_dim
 constexpr int kPThreads = 256;
 constexpr float kRescaleLog2 = 8.f;  // lazy-rescale threshold, log2 units
 
-__device__ __forceinline__ f32x4_t mfma16x16x32(const uint4& a, const uint4& b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
-                                                 0, 0, 0);
-}
-
-// Byte offset of 16-byte chunk c of row r in a swizzled 64 x 256 B tile.
-// K: chunk c ^ (r % 16) -- conflict-free for 16 rows reading one chunk.
-// V: chunk c ^ 2 (r % 8) -- conflict-free for the transposed 8-byte reads.
-__device__ __forceinline__ uint32_t k_off(int r, int c) { return r * 256 + ((c ^ (r & 15)) << 4); }
-__device__ __forceinline__ uint32_t v_off(int r, int c) { return r * 256 + ((c ^ ((r & 7) << 1)) << 4); }
 
 // Workgroup barrier that does not drain outstanding loads (the tile DMA must
 // stay in flight across it): this wave's LDS reads are complete, then
@@ -86,14 +72,6 @@ __device__ __forceinline__ void barrier_keep_loads() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Wait until at most N vector-memory instructions of this wave are
-// outstanding (s_waitcnt vmcnt(N); expcnt and lgkmcnt left alone). Issued
-// through the builtin so that the compiler's own wait bookkeeping sees it.
-template <int N>
-__device__ __forceinline__ void wait_vmem_le() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
 
 template <int B>
 using Buf = std::integral_constant<int, B>;
@@ -108,7 +86,6 @@ __device__ __forceinline__ void static_for_from(F&& f) {
 template <int N, class F>
 __device__ __forceinline__ void static_for(F&& f) { static_for_from<0, N>(f); }
 
-typedef int v2i_t __attribute__((ext_vector_type(2)));
 
 // Opaque re-definition of register values (no instruction is emitted).
 template <int N>
@@ -117,16 +94,6 @@ __device__ __forceinline__ void launder(uint32_t (&x)[N]) {
   for (int i = 0; i < N; ++i) asm volatile("" : "+v"(x[i]));
 }
 
-// Maximum of x over lanes l and l ^ 16 (l ^ 32): the row-swap permutes put
-// each lane's partner value in one of the two results.
-__device__ __forceinline__ float max_xor16(float x) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float max_xor32(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
 
 // kRawMax: the scale is positive, so the running maximum is taken on raw
 // scores and the scale folds into the exponent's FMA; otherwise scores are
