@@ -9,8 +9,8 @@
 // (page "nano-vLLM 最小化vLLM重新实现", section 5 "注意力机制": decode attention
 // over the paged KV cache; section 3 "块管理器": fixed-size blocks).
 //
-// Design for gfx950 (HBM-bound; vector arithmetic for 1, 2 and 4 query heads
-// per kv head, the matrix cores at 8, see decode_mfma_kernel):
+// Design for gfx950 (HBM-bound; vector arithmetic for 1 and 2 query heads per
+// kv head, the matrix cores from 4 on, see decode_mfma_kernel):
 // * Work is split stream-K style. The (sequence, kv head) pairs are laid end
 //   to end as runs of chunks of 8*TPL tokens, and each of `num_waves`
 //   one-wave workgroups takes an equal share of that chunk sequence, so all
@@ -537,37 +537,45 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
 //
 // With G query heads per kv head the decode is a small dense contraction: G
 // query rows against every key of the pair. The kernel above does it with
-// vector dot products, whose cost grows with G until, at G = 8, the vector
-// work rather than HBM sets the time. This kernel runs the same stream-K
-// split (32-token chunks) on the MFMA units, with the G queries as the
-// columns of 16x16x32 bf16 tiles (columns G..15 are zero and ignored):
-//   Sᵀ (32 keys x 16 queries) = K Qᵀ: K rows straight from global memory into
-//     the A operand (lane (g, c): key c of a 16-key tile, dims 32 ks + 8 g ..
-//     + 7), Qᵀ held in registers;
-//   online softmax in log2 units per query column, rescaled lazily (when a
-//     column's maximum grows by more than 2^8), p in fp32;
-//   Oᵀ (128 dims x 16 queries) += Vᵀ Pᵀ: V staged in LDS by DMA (two 8 KiB
-//     buffers, the next chunk in flight) and read transposed; P is split into
-//     bf16 high and low parts (p = hi + lo to 2^-16) and both are multiplied,
-//     so the weights keep close to fp32 precision; the row sums are the fp32
-//     sums of p.
+// vector dot products, whose cost grows with G; from G = 4 on, this kernel
+// runs the same stream-K split (32-token chunks) on the MFMA units instead,
+// with the G queries as the columns of 16x16x32 bf16 tiles (columns G..15
+// are zero and ignored):
+// * Each chunk's K and V rows are loaded as whole 128-byte lines (8 rows of
+//   a 16-byte piece per lane and instruction) into a register set while the
+//   previous chunk is computed; reading K straight into the MFMA operand
+//   layout (16 rows x 64 bytes per instruction) measured 10% slower.
+// * The chunk is then written to a wave-private LDS tile (swizzled like the
+//   prefill's) and read back as operands: K rows for Sᵀ = K Qᵀ (Qᵀ held in
+//   registers), V transposed with ds_read_b64_tr_b16 for Oᵀ += Vᵀ Pᵀ.
+// * Online softmax in log2 units per query column, rescaled lazily (when a
+//   column's maximum grows by more than 2^8), p in fp32; P is split into
+//   bf16 high and low parts (p = hi + lo to 2^-16) and both are multiplied,
+//   so the weights keep close to fp32 precision; the row sums are the fp32
+//   sums of p.
 // Pieces go to the same workspace slots, in the same (max, sum, output)
 // format, and the same finalize pass combines them.
 template <int G>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int CH = 32;  // tokens per chunk
   static_assert(G <= 16, "the queries of a kv head are the columns of one 16-column tile");
-  __shared__ __attribute__((aligned(1024))) char vbuf0[CH * 256];
-  __shared__ __attribute__((aligned(1024))) char vbuf1[CH * 256];
+  // the chunk being computed, re-laid out for the operand reads (wave-private)
+  __shared__ __attribute__((aligned(1024))) char ksh[CH * 256];
+  __shared__ __attribute__((aligned(1024))) char vsh[CH * 256];
   const int wave = blockIdx.x, lane = threadIdx.x;
-  const int g = lane >> 4, col = lane & 15;
+  const int g = lane >> 4, col = lane & 15;  // MFMA operand lanes
+  const int r8 = lane >> 3, s8 = lane & 7;   // load lanes: row r8 + 8 q % 4 of the chunk, 16-byte piece s8
   int ns;
   int64_t lo, hi;
   Pos cur;
   if (!locate_share(a, CH, wave, lane, ns, lo, hi, cur)) return;
 
   const int64_t row_elems = (int64_t)a.num_kv_heads * kD;  // elements between tokens' rows in the cache
-  // Vᵀ operand reads: lane (g, c) takes dims 16 dt + c of keys 4 g .. 4 g + 3 (low half) and 16 + 4 g .. (high)
+  // K operand reads: lane (g, col) takes key col of a 16-key tile, dims 32 ks + 8 g .. + 7
+  uint32_t koff[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) koff[ks] = k_off(col, ks * 4 + g);
+  // Vᵀ operand reads: dims 16 dt + col of keys 4 g .. 4 g + 3 (low half) and 16 + 4 g .. (high)
   uint32_t voff[8];
   {
     const int trow = 4 * g + (col >> 2), tq = col & 3;
@@ -575,11 +583,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
     for (int dt = 0; dt < 8; ++dt) voff[dt] = v_off(trow, 2 * dt + (tq >> 1)) + (tq & 1) * 8;
   }
 
-  // Issue the loads of chunk p: K rows into kreg (A operand layout), V rows by
-  // DMA into vbuf (row-major, swizzled). Rows past the context end are read
-  // from the last token (their scores are masked; their V rows must be
-  // finite); the new token (pa_store_decode) comes from k_new / v_new.
-  auto issue = [&](const Pos& p, uint4 (&kreg)[2][4], char* vbuf) {
+  // Loads of chunk p into registers, whole 128-byte lines per instruction:
+  // load q (< 8) takes row r8 + 8 (q % 4), 16-byte piece 8 (q / 4) + s8. Rows
+  // past the context end are read from the last token (their scores are
+  // masked; their V rows must be finite); the new token (pa_store_decode)
+  // comes from k_new / v_new.
+  struct ChunkKV {
+    uint4 k[8], v[8];
+  };
+  auto issue = [&](const Pos& p, ChunkKV& c) {
     const int tok0 = p.k * CH;
     const int nvalid = min(CH, p.len - tok0);
     const int blk = a.block_tables[(int64_t)p.b * a.max_blocks_per_seq + tok0 / a.block_size];
@@ -587,23 +599,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
     const bool has_new = a.k_new != nullptr;
     const int new_row = p.len - 1 - tok0;  // row of the new token in this chunk (if < CH)
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int row = min(16 * t + col, nvalid - 1);
-      const uint16_t* kr = (has_new && row == new_row) ? a.k_new + p.b * a.k_new_stride + p.g * kD
-                                                       : a.k_cache + base + row * row_elems;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) kreg[t][ks] = load16_nt(kr + 32 * ks + 8 * g);
-    }
-    // DMA instruction u fills rows 4u .. 4u + 3: lane (g, c) supplies row
-    // 4u + g, physical chunk c, i.e. the logical chunk the V swizzle puts there
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int row = min(4 * u + g, nvalid - 1);
-      const int chunk = col ^ (((4 * u + g) & 7) << 1);
-      const uint16_t* vr = (has_new && row == new_row) ? a.v_new + p.b * a.v_new_stride + p.g * kD
-                                                       : a.v_cache + base + row * row_elems;
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(vr) + 16 * chunk, (lds_void_t*)(vbuf + u * 1024),
-                                       16, 0, 0);
+    for (int q = 0; q < 8; ++q) {
+      const int row = min(r8 + 8 * (q & 3), nvalid - 1);
+      const int e = 64 * (q >> 2) + 8 * s8;
+      const bool nw = has_new && row == new_row;
+      c.k[q] = load16_nt((nw ? a.k_new + p.b * a.k_new_stride + p.g * kD : a.k_cache + base + row * row_elems) + e);
+      c.v[q] = load16_nt((nw ? a.v_new + p.b * a.v_new_stride + p.g * kD : a.v_cache + base + row * row_elems) + e);
     }
   };
 
@@ -631,14 +632,29 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
   const float c = a.scale_log2e;
   constexpr float tau = 8.f;  // lazy-rescale threshold, log2 units
 
-  // One chunk: scores, softmax, Vᵀ Pᵀ. more: the next chunk's 16 loads are in flight.
-  auto compute = [&](const Pos& p, const uint4 (&kreg)[2][4], const char* vbuf, bool more) {
+  // One chunk: stage it in LDS, scores, softmax, Vᵀ Pᵀ.
+  auto compute = [&](const Pos& p, const ChunkKV& kv) {
     const int nvalid = min(CH, p.len - p.k * CH);
+    // Every read of the previous chunk precedes these writes in the wave's
+    // program order and LDS operations of one wave complete in order; the
+    // fences keep the compiler from moving accesses across.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int row = r8 + 8 * (q & 3), piece = 8 * (q >> 2) + s8;
+      *reinterpret_cast<uint4*>(ksh + k_off(row, piece)) = kv.k[q];
+      *reinterpret_cast<uint4*>(vsh + v_off(row, piece)) = kv.v[q];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     f32x4_t sacc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-      for (int t = 0; t < 2; ++t) sacc[t] = mfma16x16x32(kreg[t][ks], qop[ks], sacc[t]);
+      for (int t = 0; t < 2; ++t)
+        sacc[t] = mfma16x16x32(*reinterpret_cast<const uint4*>(ksh + t * 16 * 256 + koff[ks]), qop[ks], sacc[t]);
     // lane (g, col): query col, keys 16 t + 4 g + i
     float x[2][4];
 #pragma unroll
@@ -686,11 +702,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
       }
     const uint4 poph = make_uint4(ph[0], ph[1], ph[2], ph[3]);
     const uint4 popl = make_uint4(pl[0], pl[1], pl[2], pl[3]);
-    // the chunk's V DMA has landed once at most the next chunk's 16 loads are outstanding
-    if (more) wait_vmem_le<16>(); else wait_vmem_le<0>();
-    asm volatile("" ::: "memory");
     typedef __attribute__((address_space(3))) const char lds_char_t;
-    lds_char_t* vl = (lds_char_t*)vbuf;
+    lds_char_t* vl = (lds_char_t*)vsh;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
       const s16x4_t l4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vl + voff[dt]));
@@ -727,12 +740,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
     }
   };
 
-  uint4 kA[2][4], kB[2][4];
-  issue(cur, kA, vbuf0);
+  ChunkKV cA, cB;
+  issue(cur, cA);
   load_qop(cur);
   reset();
   int k0 = cur.k;  // first chunk of the current piece
-  // two stages with the register sets and LDS buffers swapped
+  // two stages with the register sets swapped: the next chunk's loads are in
+  // flight while the current one is computed
   for (int64_t ci = lo;;) {
     {
       const bool more = ci + 1 < hi;
@@ -741,9 +755,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
       if (more) {
         nxt = next_pos(cur, a, CH, ns);
         new_pair = nxt.b != cur.b || nxt.g != cur.g;
-        issue(nxt, kB, vbuf1);
+        issue(nxt, cB);
       }
-      compute(cur, kA, vbuf0, more);
+      compute(cur, cA);
       if (!more || new_pair) {
         finish(cur, k0);
         if (!more) break;
@@ -761,9 +775,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
       if (more) {
         nxt = next_pos(cur, a, CH, ns);
         new_pair = nxt.b != cur.b || nxt.g != cur.g;
-        issue(nxt, kA, vbuf0);
+        issue(nxt, cA);
       }
-      compute(cur, kB, vbuf1, more);
+      compute(cur, cB);
       if (!more || new_pair) {
         finish(cur, k0);
         if (!more) break;
@@ -907,18 +921,19 @@ __global__ __launch_bounds__(64) void decode_finalize_kernel(DecodeArgs a) {
   }
 }
 
-// G = 8 takes the split pass on the matrix cores. Same-box timings of the
-// two split passes (config-2 lengths at Hkv = 8; 512 long contexts at G = 4):
-// G = 8 370 us vector, 237 us matrix; G = 4 213 / 224 us and 2286 / 2321 us.
-constexpr int kMfmaMinGroup = 8;
+// G >= 4 take the split pass on the matrix cores. Same-box timings (us) of
+// the vector pass against the matrix pass: config-2 lengths at Hkv = 8, G = 4
+// 207.9 / 196.3 and G = 8 370 / 198.5 (the vector pass at G = 8 spilled and
+// ran one wave per SIMD); 512 long contexts at G = 4 2322.9 / 2268.8; G = 2
+// 196.9 / 196.8, so G <= 2 keep the vector pass.
+constexpr int kMfmaMinGroup = 4;
 
-// Vector split pass: tokens per lane per chunk 4 while the G heads' state is
-// small, else 2, so that two waves fit per SIMD. Matrix split pass: 32-token
-// chunks.
+// Vector split pass: 4 tokens per lane per chunk (32-token chunks). Matrix
+// split pass: 32-token chunks.
 template <int G>
 static hipError_t launch_decode_g(const DecodeArgs& a, hipStream_t stream) {
   constexpr bool kMfma = G >= kMfmaMinGroup;
-  constexpr int TPL = (kMfma || G <= 2) ? 4 : 2;  // the finalize pass's chunk: 8 TPL tokens
+  constexpr int TPL = 4;  // the finalize pass's chunk: 8 TPL tokens
   if constexpr (kMfma) decode_mfma_kernel<G><<<dim3(a.num_waves), dim3(64), 0, stream>>>(a);
   else decode_split_kernel<G, TPL><<<dim3(a.num_waves), dim3(64), 0, stream>>>(a);
   hipError_t e = hipGetLastError();
@@ -927,7 +942,7 @@ static hipError_t launch_decode_g(const DecodeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-int decode_chunk_tokens(int group) { return (group >= kMfmaMinGroup || group <= 2) ? 32 : 16; }
+int decode_chunk_tokens(int) { return 32; }
 
 hipError_t launch_decode(const DecodeArgs& a, int group, hipStream_t stream) {
   if (a.num_seqs == 0) return hipSuccess;

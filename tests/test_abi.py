@@ -187,8 +187,9 @@ def test_decode_workspace_size(lib):
     assert lib.pa_decode_split_waves(4, 16, 8, 200, 256) == 224
     assert lib.pa_decode_workspace_size(4, 16, 8, 128, 200, 256) == 224 * 2 * 2 * 130 * 4
     # G = 4: 16-token chunks; by default at least 4 chunks per wave by the length bound (1 x 8 x 7 = 56 -> 14)
-    assert lib.pa_decode_split_waves(1, 32, 8, 100, 0) == 14
-    assert lib.pa_decode_split_waves(1, 64, 8, 100, 0) == 8  # G = 8: 32-token chunks on the matrix cores
+    # 32-token chunks at every group size: 4 chunks x 8 kv heads, at least 4 chunks per wave
+    assert lib.pa_decode_split_waves(1, 32, 8, 100, 0) == 8
+    assert lib.pa_decode_split_waves(1, 64, 8, 100, 0) == 8
     # a small batch under the bound: 16 x 8 x 64 = 8192 chunks -> 2048 waves; 1 x 8 x 64 = 512 -> 128
     assert lib.pa_decode_split_waves(16, 16, 8, 2048, 0) == 2048
     assert lib.pa_decode_split_waves(1, 16, 8, 2048, 0) == 128
