@@ -160,10 +160,12 @@ int32_t pa_decode_split_waves(int32_t num_seqs, int32_t num_q_heads, int32_t num
  * block_tables[b, t / block_size], kv head h / G. L counts the token just
  * stored, so a new token attends to itself. L == 0 gives a zero row.
  * Arithmetic: bf16 inputs, fp32 accumulation and softmax, bf16 output
- * (round to nearest even).
+ * (round to nearest even). From G >= 4 the two products run on the matrix
+ * cores, the softmax weights entering the second as two bf16 parts (about 16
+ * significant bits).
  *
  * Work split: the (sequence, kv head) pairs are cut into chunks of 32 tokens
- * (16 when G >= 4) and the chunk sequence is shared equally among
+ * and the chunk sequence is shared equally among
  * split_waves waves; a pair cut by a share boundary is finished by a second,
  * small kernel from fp32 partials (max, sum, unnormalised output) in the
  * workspace (the split-K partition-and-reduce).
