@@ -62,6 +62,17 @@ def test_decode_config2_splits(dev, waves):
     _run(configs.config2(), dev, split_waves=waves)
 
 
+@pytest.mark.parametrize("group", [4, 8])
+@pytest.mark.parametrize("waves", [0, 1, 7, 300, 5000])
+def test_decode_matrix_core_splits(dev, group, waves):
+    # the matrix-core split pass (G >= 4) over 64 sequences of config-2 lengths: 1 wave holds every pair whole,
+    # 7..5000 waves cut pairs across 2 to many waves
+    announce(f"decode G={group} split over {waves} waves")
+    lens = np.random.default_rng([2, 0]).integers(100, 2048, size=64, endpoint=True)
+    wl = configs.decode_workload(f"g{group}-64seq", lens, 8 * group, 8, 1024, 2)
+    _run(wl, dev, split_waves=waves)
+
+
 def test_decode_config5_sampled(dev):
     announce("decode config 5, sampled sequences")
     wl = configs.config5()

@@ -28,9 +28,15 @@ pytestmark = pytest.mark.gpu
 SIZES = [1, 2, 4, 8, 16, 32, 64, 128, 256, 512]
 
 
-def test_decode_graphs_match_eager_and_oracle(dev):
-    announce("decode graphs 1..512 vs eager")
-    wl = configs.config2()  # 256 sequences, L ~ U{100..2048}, 4096-block pool (about 1200 used)
+@pytest.mark.parametrize("hq", [16, 64])
+def test_decode_graphs_match_eager_and_oracle(dev, hq):
+    # 16 query heads: the vector split pass; 64 (8 per kv head): the matrix-core split pass
+    announce(f"decode graphs 1..512 vs eager, {hq} query heads")
+    if hq == 16:
+        wl = configs.config2()  # 256 sequences, L ~ U{100..2048}, 4096-block pool (about 1200 used)
+    else:
+        lens = np.random.default_rng([2, 0]).integers(100, 2048, size=256, endpoint=True)
+        wl = configs.decode_workload("cfg2-g8", lens, hq, 8, 4096, 2)
     b = tensors.materialize(wl, dev)
     scale = 1.0 / math.sqrt(128)
     w = int(b.block_tables.shape[1])
@@ -39,19 +45,19 @@ def test_decode_graphs_match_eager_and_oracle(dev):
     canary = wl.num_blocks - 1  # a block no sequence of the batch uses
     assert canary not in set(wl.block_tables.ravel().tolist())
     # the step's fixed buffers
-    q_s = torch.randn((maxb, 16, 128), device=dev).to(torch.bfloat16)
+    q_s = torch.randn((maxb, hq, 128), device=dev).to(torch.bfloat16)
     k_s = torch.randn((maxb, 8, 128), device=dev).to(torch.bfloat16)
     v_s = torch.randn((maxb, 8, 128), device=dev).to(torch.bfloat16)
     bt_s = torch.full((maxb, w), canary, dtype=torch.int32, device=dev)
     cl_s = torch.full((maxb,), 777, dtype=torch.int32, device=dev)  # stale lengths past every batch
-    out_s = torch.empty((maxb, 16, 128), dtype=torch.bfloat16, device=dev)
-    ws = torch.empty(pa.pa_decode_workspace_size(maxb, 16, 8, 128, max_len), dtype=torch.uint8, device=dev)
+    out_s = torch.empty((maxb, hq, 128), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(pa.pa_decode_workspace_size(maxb, hq, 8, 128, max_len), dtype=torch.uint8, device=dev)
     canary_k, canary_v = b.k_cache[canary].clone(), b.v_cache[canary].clone()
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
         graphs = pa.DecodeGraphs(q_s, k_s, v_s, bt_s, cl_s, out_s, ws, b.k_cache, b.v_cache, scale, max_len,
                                  SIZES)
-        ws_e = torch.empty(pa.pa_decode_workspace_size(maxb, 16, 8, 128, max_len), dtype=torch.uint8, device=dev)
+        ws_e = torch.empty(pa.pa_decode_workspace_size(maxb, hq, 8, 128, max_len), dtype=torch.uint8, device=dev)
         checked_oracle = False
         for batch in (1, 3, 17, 100, 255, 256):
             rows = torch.arange(batch, device=dev)
@@ -84,7 +90,7 @@ def test_decode_graphs_match_eager_and_oracle(dev):
                 host = Compact(b, seqs)  # the new tokens are in the cache already (stored by the replays)
                 want = oracle.decode(tensors.to_u16(b.q[:batch]), host.k, host.v, host.tables,
                                      wl.context_lens[:batch], scale)
-                assert_attention_close(got, want, "graph decode, 17 sequences")
+                assert_attention_close(got, want, f"graph decode, 17 sequences, {hq} query heads")
                 checked_oracle = True
         graphs.close()
 
