@@ -602,9 +602,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
     for (int q = 0; q < 8; ++q) {
       const int row = min(r8 + 8 * (q & 3), nvalid - 1);
       const int e = 64 * (q >> 2) + 8 * s8;
-      const bool nw = has_new && row == new_row;
-      c.k[q] = load16_nt((nw ? a.k_new + p.b * a.k_new_stride + p.g * kD : a.k_cache + base + row * row_elems) + e);
-      c.v[q] = load16_nt((nw ? a.v_new + p.b * a.v_new_stride + p.g * kD : a.v_cache + base + row * row_elems) + e);
+      const bool is_new = has_new && row == new_row;
+      c.k[q] = load16_nt((is_new ? a.k_new + p.b * a.k_new_stride + p.g * kD : a.k_cache + base + row * row_elems) + e);
+      c.v[q] = load16_nt((is_new ? a.v_new + p.b * a.v_new_stride + p.g * kD : a.v_cache + base + row * row_elems) + e);
     }
   };
 
