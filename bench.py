@@ -294,7 +294,8 @@ def decode_source_sha() -> str:
     """Hash of the decode kernels' sources and build flags: a recorded counter figure is only
     reported while it still describes the code being run."""
     import hashlib
-    srcs = [os.path.join(ROOT, "paged_kv_cache_heads_amd", "csrc", n) for n in ("decode.hip", "common.h")]
+    srcs = [os.path.join(ROOT, "paged_kv_cache_heads_amd", "csrc", n)
+            for n in ("decode.hip", "common.h", "launch.h", "mfma_tiles.h")]
     srcs.append(os.path.join(ROOT, "paged_kv_cache_heads_amd", "build.py"))
     return hashlib.sha256(b"".join(open(p, "rb").read() for p in srcs)).hexdigest()[:16]
 
