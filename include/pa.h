@@ -24,12 +24,16 @@
  *   positive multiple of 64 (the pages' default is 256 and they require a
  *   multiple of 256: page "nano-vLLM 最小化vLLM重新实现", "关键设计选择").
  *   All pointers and row strides must be 16-byte aligned.
- * - Ownership: the caller owns every buffer. The library allocates nothing,
- *   keeps no pointer after return and has no global mutable state. Work is
- *   enqueued on `stream` (a hipStream_t; NULL = the null stream) and the call
- *   returns without synchronising; buffers must stay alive until the stream
- *   has run the work. No entry point reads device memory from the host, so
- *   all of them may be recorded into a HIP graph.
+ * - Ownership: the caller owns every buffer. The compute entry points
+ *   allocate nothing and keep no pointer after return. The exceptions are
+ *   named where they are declared: the host objects made by
+ *   pa_decode_graphs_create and the block manager (pa_blocks.h), which hold
+ *   what they are given until destroyed, and the static device scratch of
+ *   pa_store_decode_noalloc. Work is enqueued on `stream` (a hipStream_t;
+ *   NULL = the null stream) and the call returns without synchronising;
+ *   buffers must stay alive until the stream has run the work. No entry point
+ *   reads device memory from the host, so all of them may be recorded into a
+ *   HIP graph.
  * - Errors: arguments are checked on the host before anything is launched; a
  *   failed check returns a non-zero pa_status and launches nothing. A launch
  *   failure returns PA_ERR_HIP. pa_last_error() gives a message for the most
@@ -310,10 +314,10 @@ int pa_prefill_varlen(void* out, const void* q, int64_t q_token_stride, const vo
  * offset mod 2^32, offset div 2^32). The block's 32-bit words w0..w3 form
  * X0 = w1:w0 and X1 = w3:w2; fields 0, 1, 2 are bits 63..43, 42..22, 21..1 of
  * X0 and fields 3, 4, 5 the same bits of X1; a field w gives u = (w + 1/2) /
- * 2^21. Pass a new offset (e.g. the step number) for new noise. The decision is taken in fp32 (l log2(e) / T - log2(-log2(u))); ties
- * go to the lowest index; -inf logits are never drawn unless a whole row is
- * -inf (then token 0 by the tie rule); NaN logits give an unspecified token in
- * [0, vocab_size).
+ * 2^21. Pass a new offset (e.g. the step number) for new noise. The decision
+ * is taken in fp32 (l log2(e) / T - log2(-log2(u))); ties go to the lowest
+ * index; -inf logits are never drawn unless a whole row is -inf (then token 0
+ * by the tie rule); NaN logits give an unspecified token in [0, vocab_size).
  *
  * tokens        [num_rows] int32 (device).
  * logits        [num_rows, vocab_size] fp32, rows logits_row_stride elements
