@@ -290,13 +290,15 @@ def measured_peaks(torch, dev):
             "note": "1 GiB device copy (read + write bytes); torch.matmul bf16 8192^3; best of 10"}
 
 
+# The decode kernels' source and every local header it includes (csrc/), then the build flags.
+DECODE_SOURCES = ("csrc/decode.hip", "csrc/common.h", "csrc/launch.h", "csrc/mfma_tiles.h", "build.py")
+
+
 def decode_source_sha() -> str:
     """Hash of the decode kernels' sources and build flags: a recorded counter figure is only
     reported while it still describes the code being run."""
     import hashlib
-    srcs = [os.path.join(ROOT, "paged_kv_cache_heads_amd", "csrc", n)
-            for n in ("decode.hip", "common.h", "launch.h", "mfma_tiles.h")]
-    srcs.append(os.path.join(ROOT, "paged_kv_cache_heads_amd", "build.py"))
+    srcs = [os.path.join(ROOT, "paged_kv_cache_heads_amd", n) for n in DECODE_SOURCES]
     return hashlib.sha256(b"".join(open(p, "rb").read() for p in srcs)).hexdigest()[:16]
 
 

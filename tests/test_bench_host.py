@@ -86,3 +86,22 @@ def test_oracle_baselines_on_a_worker_pool():
     finally:
         pool.terminate()
         pool.join()
+
+
+def test_traffic_gate_hashes_every_decode_source():
+    """The recorded decode traffic is reported only while the decode kernels' sources hash to the
+    recorded value; every local header decode.hip pulls in (recursively) must be part of that hash."""
+    import re
+    csrc = os.path.join(ROOT, "paged_kv_cache_heads_amd", "csrc")
+    seen, todo = set(), ["decode.hip"]
+    while todo:
+        name = todo.pop()
+        if name in seen:
+            continue
+        seen.add(name)
+        for inc in re.findall(r'^#include "([^"]+)"', open(os.path.join(csrc, name)).read(), re.M):
+            if not inc.startswith("../"):
+                todo.append(inc)
+    assert {"csrc/" + n for n in seen} <= set(bench.DECODE_SOURCES), seen
+    assert "build.py" in bench.DECODE_SOURCES
+    assert len(bench.decode_source_sha()) == 16
