@@ -85,10 +85,10 @@ def test_decode_config5_sampled(dev):
 
 
 @pytest.mark.parametrize("group", [1, 2, 4, 8])
-@pytest.mark.parametrize("block_size", [64, 256])
+@pytest.mark.parametrize("block_size", [64, 192, 256])
 def test_decode_edge_lengths(dev, group, block_size):
-    # empty context, one token, chunk and share boundaries, a ragged tail
-    lens = [0, 1, 2, 63, 64, 65, 255, 256, 257, 511, 512, 513, 1000, 1537]
+    # empty context, one token, chunk, block and share boundaries (192: blocks that are not a power of two), a ragged tail
+    lens = [0, 1, 2, 63, 64, 65, 191, 192, 193, 255, 256, 257, 383, 384, 385, 511, 512, 513, 1000, 1537]
     announce(f"decode edge lengths G={group} bs={block_size}")
     hkv = 2
     wl = configs.decode_workload("edge", lens, hkv * group, hkv, 128, seed=9, block_size=block_size)

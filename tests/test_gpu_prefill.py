@@ -94,12 +94,14 @@ def test_prefill_ragged_small(dev, group, causal, max_k):
 
 
 @pytest.mark.parametrize("max_k", [1, 4096])
-@pytest.mark.parametrize("block_size", [64, 256])
+@pytest.mark.parametrize("block_size", [64, 192, 256])
 @pytest.mark.parametrize("group", [2, 4])
 def test_prefill_prefix_small(dev, block_size, group, max_k):
-    # fewer queries than keys: queries are the last positions; prefix blocks shared
+    # fewer queries than keys: queries are the last positions; prefix blocks shared (the prefix is the
+    # whole blocks covering 256 tokens: 384 at block size 192)
     announce(f"prefill prefix bs={block_size} G={group} max_k={max_k}")
-    wl = configs.prefill_workload("prefix", [1, 5, 64, 100, 200], 256, 2 * group, 2, 64, seed=22,
+    prefix = -(-256 // block_size) * block_size
+    wl = configs.prefill_workload("prefix", [1, 5, 64, 100, 200], prefix, 2 * group, 2, 64, seed=22,
                                   block_size=block_size)
     _table(wl, dev, causal=True, max_k=max_k)
     _table(wl, dev, causal=False, max_k=max_k)

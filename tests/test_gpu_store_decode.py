@@ -58,10 +58,10 @@ def test_store_decode_config2(dev, split_waves):
 
 
 @pytest.mark.parametrize("group", [1, 2, 4, 8])
-@pytest.mark.parametrize("block_size", [64, 256])
+@pytest.mark.parametrize("block_size", [64, 192, 256])
 def test_store_decode_edge_lengths(dev, group, block_size):
     # empty context (nothing stored), one token (the stored row alone), chunk and block edges
-    lens = [0, 1, 2, 63, 64, 65, 255, 256, 257, 511, 512, 513, 1000, 1537]
+    lens = [0, 1, 2, 63, 64, 65, 191, 192, 193, 255, 256, 257, 383, 384, 385, 511, 512, 513, 1000, 1537]
     announce(f"store+decode edge lengths G={group} bs={block_size}")
     hkv = 2
     wl = configs.decode_workload("edge", lens, hkv * group, hkv, 128, seed=19, block_size=block_size)

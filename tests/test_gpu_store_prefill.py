@@ -83,7 +83,7 @@ def test_fused_prefix_workload(dev):
     assert_attention_close(out, ref, f"pa_store_prefill_varlen {wl.name}")
 
 
-@pytest.mark.parametrize("block_size", [64, 256])
+@pytest.mark.parametrize("block_size", [64, 192, 256])
 @pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("group", [1, 2, 4, 8])
 def test_fused_chunked_prefill_cached_part_ends_mid_tile(dev, group, causal, block_size):
