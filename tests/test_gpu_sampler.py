@@ -139,3 +139,33 @@ def test_sampler_ties_across_layouts(dev):
         lg[r, idx] = np.inf
     got = _run(lg, np.ones(len(cases)), 3, 4, dev)
     assert got.tolist() == [min(c) for c in cases]
+
+
+@pytest.mark.parametrize("pad", [8, 1])
+def test_sampler_batch_strided(dev, pad):
+    # a decode-sized batch of 256 rows, 16-byte aligned with a ragged end (pad 8) or not aligned at all
+    # (pad 1), with masked tokens; the padding never read
+    announce(f"sampler 256 x 20000 pad {pad}")
+    rng = np.random.default_rng(40 + pad)
+    rows, vocab = 256, 20000
+    logits = (rng.standard_normal((rows, vocab)) * 2).astype(np.float32)
+    logits[::5, rng.integers(0, vocab, 3000)] = -np.inf
+    temps = rng.uniform(0.3, 1.8, rows).astype(np.float32)
+    got = _run_strided(logits, temps, 77, 9, dev, pad)
+    assert np.all((got >= 0) & (got < vocab))
+    _check(got, logits.astype(np.float64), temps, 77, 9)
+
+
+def test_sampler_batch_ties_far_apart(dev):
+    # exact ties in a 256-row batch over a 100003-token vocabulary: the lowest index wins across a wave's
+    # 768-logit spans, across workgroups' 12288-logit chunks far apart in the row, and between the
+    # vector-loaded part and the ragged end
+    announce("sampler ties far apart")
+    rows, vocab = 256, 100003
+    cases = [[9, 10, 11], [767, 768], [12287, 12288], [49151, 49152], [1, 49152], [98303, 98304],
+             [49152, 100002], [100001, 100002], [5, 100002], [60000, 20000]]
+    lg = np.random.default_rng(12).standard_normal((rows, vocab)).astype(np.float32)
+    for r in range(rows):
+        lg[r, cases[r % len(cases)]] = np.inf
+    got = _run(lg, np.ones(rows), 3, 4, dev)
+    assert got.tolist() == [min(cases[r % len(cases)]) for r in range(rows)]
