@@ -96,6 +96,21 @@ def test_decode_edge_lengths(dev, group, block_size):
         _run(wl, dev, split_waves=waves)
 
 
+@pytest.mark.parametrize("group", [2, 4])
+@pytest.mark.parametrize("waves", [0, 77, 3000])
+def test_decode_many_sequences(dev, group, waves):
+    # 1500 short contexts (empty ones among them): the length scans of the split and finalize kernels walk six
+    # 256-sequence windows, and pairs are cut across every window boundary
+    announce(f"decode 1500 sequences G={group} waves={waves}")
+    lens = np.random.default_rng(70 + group).integers(0, 300, size=1500)
+    lens[::97] = 0
+    hkv = 2
+    wl = configs.decode_workload("many", lens, hkv * group, hkv, 2000, seed=41)
+    rng = np.random.default_rng(5)
+    seqs = sorted(set([0, 255, 256, 511, 512, 1023, 1024, 1499] + [int(x) for x in rng.choice(1500, 40, replace=False)]))
+    _run(wl, dev, seqs=seqs, split_waves=waves)
+
+
 def test_decode_zero_seqs(dev):
     announce("decode with zero sequences")
     kc = torch.zeros((1, 256, 8, 128), dtype=torch.bfloat16, device=dev)
