@@ -416,25 +416,27 @@ def decode_graph_latency(pa, torch, b2, wl2, scale, batches=(1, 16, 256), iters=
     return res
 
 
-def cold_launches(torch, dev, kernels, calls, reps=10):
-    """Median event-timed duration (us) of each launch run alone after a 512 MiB write has flushed the L2
-    and MALL, so that no kernel finds its inputs left in cache by the one before it."""
+def cold_launches(torch, dev, kernels, calls, reps=20, warmup=5):
+    """Event-timed duration (us) of each launch run alone after a 512 MiB write has flushed the L2 and
+    MALL, so that no kernel finds its inputs left in cache by the one before it: `warmup` untimed calls,
+    then `reps` timed ones. Returns the medians and, separately, median / min / max."""
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-    out = {}
+    out, stats = {}, {}
     for name in kernels:
         t = []
-        for r in range(reps + 2):
+        for r in range(reps + warmup):
             flush.fill_(r & 0xFF)
             e0, e1 = TimingEvent(), TimingEvent()
             e0.record()
             calls[name]()
             e1.record()
             torch.cuda.synchronize()
-            if r >= 2:
+            if r >= warmup:
                 t.append(e0.elapsed_time(e1) * 1e3)
         out[name] = round(float(np.median(t)), 2)
+        stats[name] = {"median": out[name], "min": round(float(np.min(t)), 2), "max": round(float(np.max(t)), 2)}
     del flush
-    return out
+    return out, stats
 
 
 # ----------------------------------------------------------------------------- oracle baseline (host)
@@ -723,7 +725,7 @@ def run(args, pool, n_cores) -> dict:
     peaks = measured_peaks(torch, dev)
     # after the timed steps: each launch alone with the caches flushed first (a 512 MiB write, untimed);
     # skipped in profiling runs, whose per-kernel statistics cover the timed steps only
-    cold = None if args.step_only else cold_launches(torch, dev, kernels, calls)
+    cold, cold_stats = (None, None) if args.step_only else cold_launches(torch, dev, kernels, calls)
 
     # Each roofline also gives the launch's cold figure (run alone right after a 512 MiB write has flushed
     # L2 and MALL), the timing the protocol asks for where the working set fits in those caches.
@@ -798,6 +800,7 @@ def run(args, pool, n_cores) -> dict:
         "kernels_us": {k: round(v * 1e3, 2) for k, v in ms.items()},
         "kernels_us_stats": stats,
         "kernels_us_cold": cold,
+        "kernels_us_cold_stats": cold_stats,
         "measured_peaks": peaks,
     }
     if b5 is not None:
