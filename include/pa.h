@@ -80,16 +80,16 @@ int pa_version(void);
  * token t with slot_mapping[t] = s >= 0:
  *   k_cache[s / block_size, s % block_size, :, :] = k[t, :, :]
  *   v_cache[s / block_size, s % block_size, :, :] = v[t, :, :]
- * Tokens with a negative slot are skipped (padding).
+ * Tokens with a negative slot are skipped (padding), and so are tokens whose
+ * slot is num_blocks * block_size or more (no such slot in the cache).
  *
  * k, v          [num_tokens, num_kv_heads, head_dim] bf16; heads x dims
  *               contiguous, token rows k_token_stride / v_token_stride
  *               elements apart (>= num_kv_heads * head_dim; K and V may be
  *               column slices of a fused qkv projection output).
  * k_cache, v_cache  [num_blocks, block_size, num_kv_heads, head_dim] bf16.
- * slot_mapping  [num_tokens] int32. Non-negative slots must be
- *               < num_blocks * block_size and pairwise distinct (with a
- *               repeated slot the result is unspecified).
+ * slot_mapping  [num_tokens] int32. The slots stored to must be pairwise
+ *               distinct (with a repeated slot the result is unspecified).
  * Bytes copied are exact (bit-for-bit), NaN patterns included.
  */
 int pa_store_kvcache(const void* k, int64_t k_token_stride, const void* v, int64_t v_token_stride, void* k_cache,

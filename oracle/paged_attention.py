@@ -56,15 +56,17 @@ def store_kvcache(k, v, slot_mapping, k_cache, v_cache):
 
     ``k``, ``v``: ``[T, Hkv, D]`` uint16; caches ``[NB, bs, Hkv, D]`` uint16.
     Returns new cache arrays; the inputs are not modified. Tokens whose slot is
-    negative are skipped. Page "nano-vLLM 最小化vLLM重新实现", section 5
-    "注意力机制" (store kernel writing K/V into the paged cache by slot).
+    negative (padding) or past the last slot of the cache are skipped. Page
+    "nano-vLLM 最小化vLLM重新实现", section 5 "注意力机制" (store kernel writing
+    K/V into the paged cache by slot).
     """
     kc = np.array(k_cache, dtype=np.uint16, copy=True)
     vc = np.array(v_cache, dtype=np.uint16, copy=True)
     block_size = kc.shape[1]
+    capacity = kc.shape[0] * block_size
     for t in range(len(slot_mapping)):
         s = int(slot_mapping[t])
-        if s < 0:
+        if s < 0 or s >= capacity:
             continue
         kc[s // block_size, s % block_size] = k[t]
         vc[s // block_size, s % block_size] = v[t]

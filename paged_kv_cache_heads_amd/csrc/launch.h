@@ -24,6 +24,7 @@ struct StoreArgs {
   const int32_t* slot_mapping;
   int32_t num_tokens;
   int32_t row_vecs;  // 16-byte vectors per token row (num_kv_heads * head_dim / 8)
+  int32_t capacity;  // num_blocks * block_size: slots at or above it are skipped, like negative ones
 };
 
 struct DecodeArgs {

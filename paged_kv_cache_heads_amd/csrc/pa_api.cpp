@@ -163,6 +163,7 @@ int pa_store_kvcache(const void* k, int64_t k_token_stride, const void* v, int64
   a.slot_mapping = slot_mapping;
   a.num_tokens = num_tokens;
   a.row_vecs = (int32_t)(row / 8);
+  a.capacity = (int32_t)(num_blocks * block_size);
   return hip_status(pa::launch_store_kvcache(a, static_cast<hipStream_t>(stream)), "store_kvcache launch");
 }
 

@@ -28,7 +28,8 @@ constexpr int kStoreThreads = 256;
 constexpr int kStoreUnroll = 4;
 
 // Locate the 16-byte vector idx of the flattened (token, K row | V row) space.
-// Returns false for vectors past the end and for tokens with a negative slot.
+// Returns false for vectors past the end and for tokens whose slot is negative
+// (padding) or past the cache.
 __device__ __forceinline__ bool store_vector(const StoreArgs& a, uint32_t idx, uint32_t total, const uint4*& src,
                                              uint4*& dst) {
   if (idx >= total) return false;
@@ -36,7 +37,7 @@ __device__ __forceinline__ bool store_vector(const StoreArgs& a, uint32_t idx, u
   const uint32_t t = idx / per_token;
   uint32_t c = idx - t * per_token;
   const int32_t slot = a.slot_mapping[t];
-  if (slot < 0) return false;  // padded token: nothing to store
+  if ((uint32_t)slot >= (uint32_t)a.capacity) return false;  // padded token or no such slot: nothing to store
   const bool is_v = c >= (uint32_t)a.row_vecs;
   if (is_v) c -= a.row_vecs;
   const uint16_t* row = is_v ? a.v + (int64_t)t * a.v_token_stride : a.k + (int64_t)t * a.k_token_stride;
@@ -75,7 +76,7 @@ __global__ __launch_bounds__(kStoreThreads) void store_tokens_kernel(StoreArgs a
   const int t = (int)(blockIdx.x << (8 - vec_shift)) + (tid >> vec_shift);
   if (t >= a.num_tokens) return;
   const int32_t slot = a.slot_mapping[t];
-  if (slot < 0) return;  // padded token: nothing to store
+  if ((uint32_t)slot >= (uint32_t)a.capacity) return;  // padded token or no such slot: nothing to store
   int c = tid & ((1 << vec_shift) - 1);
   const bool is_v = c >= a.row_vecs;
   if (is_v) c -= a.row_vecs;

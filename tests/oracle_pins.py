@@ -150,12 +150,13 @@ def check_store_bruteforce(orc, seed=0):
     nb, bs, hkv, d, t = 6, 5, 2, 3, 17
     slots = rng.permutation(nb * bs)[:t].astype(np.int64)
     slots[rng.random(t) < 0.2] = -1
+    slots[[3, 8, 11]] = [nb * bs, nb * bs + 7, 2**31 - 1]  # no such slot: nothing stored
     k, v = _rand(rng, (t, hkv, d)), _rand(rng, (t, hkv, d))
     kc0 = rng.integers(0, 1 << 16, (nb, bs, hkv, d)).astype(np.uint16)
     vc0 = rng.integers(0, 1 << 16, (nb, bs, hkv, d)).astype(np.uint16)
     kc, vc = orc.store_kvcache(k, v, slots, kc0, vc0)
     want_k, want_v = kc0.reshape(nb * bs, hkv, d).copy(), vc0.reshape(nb * bs, hkv, d).copy()
-    ok = slots >= 0
+    ok = (slots >= 0) & (slots < nb * bs)
     want_k[slots[ok]] = k[ok]
     want_v[slots[ok]] = v[ok]
     assert np.array_equal(kc.reshape(nb * bs, hkv, d), want_k)

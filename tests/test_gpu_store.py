@@ -76,6 +76,33 @@ def test_store_padding_and_small_blocks(dev):
     assert np.array_equal(tensors.to_u16(batch.v_cache), vref)
 
 
+@pytest.mark.parametrize("hkv", [2, 3])
+def test_store_slots_past_the_cache(dev, hkv):
+    # slots at or past num_blocks * block_size store nothing (both kernel layouts: 2 kv heads take whole tokens per
+    # workgroup, 3 the flat one); the cache is the front of a larger buffer whose two guard blocks must stay untouched
+    announce(f"store slots past the cache, hkv {hkv}")
+    rng = np.random.default_rng([hkv, 99])
+    nb, bs, d, tokens = 6, 64, 128, 40
+    buf_k = torch.full((nb + 2, bs, hkv, d), -3, dtype=torch.int16, device=dev).view(torch.bfloat16)
+    buf_v = torch.full((nb + 2, bs, hkv, d), -4, dtype=torch.int16, device=dev).view(torch.bfloat16)
+    kc, vc = buf_k[:nb], buf_v[:nb]
+    k = torch.from_numpy(rng.integers(0, 1 << 16, size=(tokens, hkv, d), dtype=np.uint16).view(np.int16))
+    v = torch.from_numpy(rng.integers(0, 1 << 16, size=(tokens, hkv, d), dtype=np.uint16).view(np.int16))
+    k, v = k.to(dev).view(torch.bfloat16), v.to(dev).view(torch.bfloat16)
+    slots_np = rng.permutation(nb * bs)[:tokens].astype(np.int32)
+    slots_np[[1, 7, 20, 39]] = [nb * bs, nb * bs + 1, nb * bs + bs + 5, (nb + 2) * bs - 1]
+    slots_np[3] = -1
+    guard_k, guard_v = tensors.to_u16(buf_k[nb:]), tensors.to_u16(buf_v[nb:])
+    kc0, vc0 = tensors.to_u16(kc), tensors.to_u16(vc)
+    pa.pa_store_kvcache(k, v, kc, vc, torch.from_numpy(slots_np).to(dev))
+    torch.cuda.synchronize()
+    kref, vref = oracle.store_kvcache(tensors.to_u16(k), tensors.to_u16(v), slots_np, kc0, vc0)
+    assert np.array_equal(tensors.to_u16(kc), kref)
+    assert np.array_equal(tensors.to_u16(vc), vref)
+    assert np.array_equal(tensors.to_u16(buf_k[nb:]), guard_k)
+    assert np.array_equal(tensors.to_u16(buf_v[nb:]), guard_v)
+
+
 def test_store_empty(dev):
     announce("store with zero tokens")
     kc = torch.zeros((2, 64, 1, 128), dtype=torch.bfloat16, device=dev)

@@ -29,7 +29,8 @@ MUTANTS = {
     "normalise_by_max": ("/ w.sum()", "/ w.max()"),
     "store_transposed_index": ("kc[s // block_size, s % block_size] = k[t]",
                                "kc[s % block_size, s // block_size] = k[t]"),
-    "store_skips_slot_zero": ("if s < 0:", "if s <= 0:"),
+    "store_skips_slot_zero": ("if s < 0 or s >= capacity:", "if s <= 0 or s >= capacity:"),
+    "store_capacity_off_by_one": ("if s < 0 or s >= capacity:", "if s < 0 or s > capacity:"),
     "wrong_query_head": ("qb[h][None, :]", "qb[g][None, :]"),
     "gather_block_index": ("cache[int(block_list[p // block_size]), p % block_size]",
                            "cache[int(block_list[p % block_size]) if p % block_size < len(block_list) else 0, p % block_size]"),
