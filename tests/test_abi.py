@@ -286,3 +286,39 @@ def test_sampler_validation(lib):
     assert smp(ws=A + 4) == ALIGN
     assert smp(wsb=8) == WS
     assert smp(B=0, tok=None, lg=None, t=None, ws=None) == PA_OK
+
+
+@pytest.mark.parametrize("compiler,std", [("gcc", "-std=c99"), ("g++", "-std=c++17")])
+def test_headers_compile_and_link_from_c(lib, tmp_path, compiler, std):
+    """A C (and a C++) program that includes both headers, takes the address of every declared
+    entry point, links against the built library and calls two host-only functions."""
+    import shutil
+    import subprocess
+    if shutil.which(compiler) is None:
+        pytest.skip(f"{compiler} not found")
+    names = declared_functions()
+    src = ['#include "pa.h"', '#include "pa_blocks.h"', "#include <stdio.h>", "#include <string.h>",
+           "typedef void (*fn_t)(void);", "int main(void) {", "  fn_t fns[] = {"]
+    src += [f"    (fn_t){n}," for n in names]
+    src += ["  };",
+            "  for (size_t i = 0; i < sizeof(fns) / sizeof(fns[0]); ++i)",
+            "    if (!fns[i]) return 2;",
+            "  if (pa_version() < 100) return 3;",
+            "  /* a failing argument check: no GPU work, a status and a message */",
+            "  if (pa_store_kvcache(0, 0, 0, 0, 0, 0, 0, -1, 8, 128, 16, 256, 0) != PA_ERR_INVALID_ARGUMENT) return 4;",
+            "  if (strlen(pa_last_error()) == 0) return 5;",
+            '  printf("%zu entry points\\n", sizeof(fns) / sizeof(fns[0]));',
+            "  return 0;", "}"]
+    ext = ".c" if compiler == "gcc" else ".cpp"
+    c_file, exe = tmp_path / f"abi_user{ext}", tmp_path / "abi_user"
+    c_file.write_text("\n".join(src) + "\n")
+    libdir = os.path.dirname(_lib.LIB_PATH)
+    cmd = [compiler, std, "-Wall", "-Wextra", "-Werror", "-I", os.path.join(ROOT, "include"), str(c_file),
+           "-L", libdir, "-lpa", f"-Wl,-rpath,{libdir}", "-o", str(exe)]
+    if compiler == "gcc":
+        cmd.insert(2, "-pedantic")
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, (r.returncode, r.stdout, r.stderr)
+    assert r.stdout.strip() == f"{len(names)} entry points"
