@@ -38,8 +38,9 @@
  *   failed check returns a non-zero pa_status and launches nothing. A launch
  *   failure returns PA_ERR_HIP. pa_last_error() gives a message for the most
  *   recent failing call on the calling thread. Device-side preconditions
- *   (slot and table entries in range, lengths within the stated maxima) are
- *   the caller's and are not checked on the device.
+ *   (block-table entries in range, lengths within the stated maxima) are the
+ *   caller's and are not checked on the device. Slots are: every store skips
+ *   a token whose slot is negative or past the cache.
  */
 #ifndef PA_H_
 #define PA_H_
