@@ -172,3 +172,13 @@ def test_decode_pairs_cut_into_many_pieces(dev, group):
     announce(f"decode many pieces G={group}")
     wl = configs.decode_workload("pieces", [16384, 3, 700], 2 * group, 2, 72, seed=17)
     _run(wl, dev, split_waves=3000)
+
+
+@pytest.mark.parametrize("group", [2, 4])
+def test_decode_128k_context(dev, group):
+    # one 131072-token context (512 blocks in the table) beside a short one: the vector (G = 2) and matrix-core
+    # (G = 4) split passes cut each of its pairs into hundreds of pieces at the default split
+    announce(f"decode 128k context G={group}")
+    hkv = 2
+    wl = configs.decode_workload("ctx-128k", [131072, 77], hkv * group, hkv, 520, seed=29)
+    _run(wl, dev)

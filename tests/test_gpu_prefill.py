@@ -155,3 +155,34 @@ def test_prefill_last_row_equals_decode(dev):
                                 wl.cu_seqlens_q, wl.cu_seqlens_k, scale)[wl.cu_seqlens_q[1:] - 1]
     assert_attention_close(out[last], ref, "prefill last rows")
     assert_attention_close(dec, ref, "decode of the same rows")
+
+
+@pytest.mark.parametrize("max_k", [None, 1000])
+def test_prefill_one_sequence_fills_the_batch(dev, max_k):
+    # the largest prefill one 16384-token batch holds: one sequence of 16384 tokens (256 query tiles, up to 16384
+    # keys a row), at 64-key tiles (default) and 32-key tiles (the hint 1000), packed and through a 256-entry table
+    # of 64-token blocks (the kernel reloads its 64 held entries three times); sampled rows against the oracle
+    n, bs = 16384, 64
+    announce(f"prefill one {n}-token sequence max_k {max_k}")
+    wl = configs.prefill_workload("one-seq-16k", [n], 0, 16, 8, n // bs + 8, seed=23, block_size=bs)
+    batch = tensors.materialize(wl, dev)
+    scale = 1.0 / math.sqrt(wl.head_dim)
+    mk = wl.max_seqlen_k if max_k is None else max_k
+    host = Compact(batch, [0])  # pre-store contents
+    pa.pa_store_kvcache(batch.k_new, batch.v_new, batch.k_cache, batch.v_cache, batch.slot_mapping)
+    out = pa.pa_prefill_varlen(batch.q, batch.k_new, batch.v_new, batch.cu_seqlens_q, batch.cu_seqlens_k,
+                               wl.max_seqlen_q, mk, scale)
+    out_t = pa.pa_prefill_varlen(batch.q, batch.k_cache, batch.v_cache, batch.cu_seqlens_q, batch.cu_seqlens_k,
+                                 wl.max_seqlen_q, mk, scale, block_table=_cover(batch.block_tables, mk, bs))
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out_t.view(torch.int16)), "table path differs from packed path"
+    host.store(tensors.to_u16(batch.k_new), tensors.to_u16(batch.v_new), batch.slot_mapping.cpu().numpy(), bs)
+    rng = np.random.default_rng(24)
+    rows = sorted(set([0, 1, 2, 63, 64, 65, 127, 128, 1023, 1024, 4095, 4096, 8191, 8192, 16382, 16383] +
+                      [int(x) for x in rng.choice(n, 24, replace=False)]))
+    # row p of the sequence is the one query of a sequence of p + 1 keys read through the same table
+    cu_q = np.arange(len(rows) + 1, dtype=np.int64)
+    cu_k = np.concatenate([[0], np.cumsum(np.array(rows, dtype=np.int64) + 1)])
+    ref = oracle.prefill_varlen(tensors.to_u16(batch.q)[rows], host.k, host.v, cu_q, cu_k, scale, causal=True,
+                                block_table=np.repeat(host.tables[:1], len(rows), axis=0))
+    assert_attention_close(out[rows], ref, f"pa_prefill_varlen packed one-seq-16k max_k {max_k}")
